@@ -1,0 +1,213 @@
+"""Plain CPU definitions of the WhiFlash per-round route + greedy verify + emit step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+Sources (cited by page title and section):
+  [paper]  "WhiFlash: Accelerating Speculative Decoding with Token-Level
+           Cross-Paradigm Routing" (arXiv 2606.07710).
+  [router] model card "Qwen3-4B-NeuralRouter-df-e3".
+  [eagle]  model card "Qwen3-4B-EAGLE3".
+
+Readings taken where the pages leave a step open are listed beside the code
+that takes them.  Floating-point work is done in float64 from the exact input
+values; integer work is exact.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+MALFORMED_AL = 0
+MALFORMED_BONUS = -1
+
+
+# ----------------------------------------------------------------------------- logits
+
+
+def decode_logits(raw: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of stored logits.
+
+    bfloat16 is the upper half of an IEEE binary32 word, so placing its 16 bits
+    in the high half of a 32-bit word gives the same number exactly.
+    """
+    if dtype == "f32":
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(raw, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def row_argmax(raw: np.ndarray, dtype: str) -> np.ndarray:
+    """Greedy target token of every logits row: the lowest index holding the row maximum.
+
+    Greedy verification accepts a draft token when it equals the target's most
+    likely token ([router] "Evaluation": greedy decoding; [paper] §3.3.1 notes
+    that greedy decoding needs no softmax).  Definition used here, per row x:
+    t = min{ i : x[i] == max_k x[k] } under IEEE equality, so -0 and +0 tie and
+    ties go to the lowest index.  Precondition: no NaN (the pages are silent on
+    NaN logits).
+    """
+    raw = np.asarray(raw)
+    out = np.empty(raw.shape[0], np.int64)
+    for r in range(raw.shape[0]):
+        x = decode_logits(raw[r], dtype)
+        if np.isnan(x).any():
+            raise ValueError(f"row {r} holds NaN; the greedy argmax is undefined")
+        top = x.max()
+        out[r] = np.flatnonzero(x == top)[0]
+    return out
+
+
+# ----------------------------------------------------------------------------- router
+
+
+def gelu(z: np.ndarray) -> np.ndarray:
+    """Gaussian Error Linear Unit z * Phi(z) = z/2 * (1 + erf(z / sqrt 2)).
+
+    [paper] Appendix A "Neural Router Architecture" names GELU (Hendrycks and
+    Gimpel) without a formula; the exact-erf form is taken.
+    """
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def route(hidden, W1, b1, W2, b2, tau: float, dtype: str):
+    """Neural router and hardware-aware threshold.
+
+    [paper] §3.3.2: the router f_theta maps the final-layer hidden state h_t to
+    a scalar predicted gain Delta-AL = f_theta(h_t), and the decision rule
+    pi(h_t, tau_neural) picks the autoregressive drafter m_a (EAGLE-3) when
+    Delta-AL > tau_neural, else the diffusion drafter m_d (DFlash).
+    [paper] Appendix A: linear d -> m, GELU, dropout, linear m -> 1.
+    Readings: dropout is the identity at inference; b1 and b2 are present (the
+    parameter counts of the paper's router table include them), None meaning 0;
+    the threshold is strict, so Delta-AL == tau picks DFlash.
+    Returns (delta_al float64 [B], choice int32 [B]) with choice 1 = EAGLE-3 tree,
+    0 = DFlash chain.
+    """
+    h = decode_logits(hidden, dtype).reshape(np.asarray(hidden).shape)
+    w1 = decode_logits(W1, dtype).reshape(np.asarray(W1).shape)
+    w2 = decode_logits(W2, dtype).reshape(-1)
+    m = w1.shape[0]
+    bias1 = np.zeros(m) if b1 is None else np.asarray(b1, np.float32).astype(np.float64)
+    bias2 = 0.0 if b2 is None else float(np.float32(b2))
+    z = h @ w1.T + bias1                 # layer 1: [B, m]
+    g = gelu(z)                          # GELU; dropout = identity
+    delta_al = g @ w2 + bias2            # layer 2: [B]
+    choice = (delta_al > float(np.float32(tau))).astype(np.int32)
+    return delta_al, choice
+
+
+# ----------------------------------------------------------------------------- verify
+
+
+def verify_chain(t: np.ndarray, draft: np.ndarray):
+    """DFlash block acceptance under greedy verification.
+
+    [paper] §3.2: the drafted block goes back to the target for parallel
+    verification, and decoding continues from the last accepted token; §4
+    "Metrics": acceptance length counts the tokens accepted per verification
+    round.  Reading: row i of a sequence's K+1 rows is the target's prediction
+    after the first i draft tokens; the accepted prefix is the longest run
+    draft[0..n-1] == t[0..n-1], and the target's own token t[n] is emitted as
+    the bonus, so AL = n + 1.
+    t: int [B, K+1] row argmaxes; draft: int [B, K].  Returns (AL, bonus) int32 [B].
+    """
+    t = np.asarray(t)
+    draft = np.asarray(draft)
+    B, K = draft.shape
+    al = np.empty(B, np.int32)
+    bonus = np.empty(B, np.int32)
+    for b in range(B):
+        n = 0
+        while n < K and int(draft[b, n]) == int(t[b, n]):
+            n += 1
+        al[b] = n + 1
+        bonus[b] = t[b, n]
+    return al, bonus
+
+
+def _tree_one(t, parent, draft_ids, d2t, V):
+    N = len(parent)
+    Vd = len(d2t)
+    accepted = [False] * N
+    depth = [0] * N
+    accepted[0] = True
+    for u in range(1, N):
+        p = int(parent[u])
+        if not (0 <= p < u):
+            continue                      # malformed parent: node unreachable
+        did = int(draft_ids[u])
+        if not (0 <= did < Vd):
+            continue                      # id outside the draft vocabulary
+        tok = int(d2t[did])
+        if not (0 <= tok < V):
+            continue                      # table entry outside the target vocabulary
+        if accepted[p] and tok == int(t[p]):
+            accepted[u] = True
+            depth[u] = depth[p] + 1
+    best = min((u for u in range(N) if accepted[u]), key=lambda u: (-depth[u], u))
+    return depth[best] + 1, int(t[best]), best
+
+
+def verify_tree(t: np.ndarray, parent: np.ndarray, draft_ids: np.ndarray, d2t: np.ndarray, V: int):
+    """EAGLE-3 tree acceptance under greedy verification, with the d2t remap.
+
+    [paper] §3.2: the autoregressive drafter returns a tree of candidate tokens
+    for parallel verification; [eagle] "Model Description": the drafter proposes
+    ids of a fixed 32K draft vocabulary, mapped to target ids.  Readings: node 0
+    is the root (the last verified token) and row u is the target's prediction
+    after node u; node u >= 1 is accepted iff its parent p = parent[u] satisfies
+    0 <= p < u, p is accepted, and d2t[draft_ids[u]] == t[p] (ids outside the
+    draft vocabulary or table entries outside the target vocabulary never
+    match); the kept path ends at the deepest accepted node, lowest index on
+    ties; AL = its depth + 1 and the bonus is the target's token at it.
+    Returns (AL, bonus, best_node) int32 [B].
+    """
+    t = np.asarray(t)
+    B, N = np.asarray(parent).shape
+    al = np.empty(B, np.int32)
+    bonus = np.empty(B, np.int32)
+    best = np.empty(B, np.int32)
+    for b in range(B):
+        al[b], bonus[b], best[b] = _tree_one(t[b], parent[b], draft_ids[b], d2t, V)
+    return al, bonus, best
+
+
+def verify_routed(t_rows: np.ndarray, offsets: np.ndarray, choice: np.ndarray, K: int,
+                  chain_draft: np.ndarray, N: int, parent: np.ndarray, draft_ids: np.ndarray,
+                  d2t: np.ndarray, V: int):
+    """Per-sequence dispatch of a ragged batch to chain or tree acceptance.
+
+    [paper] §3.3: the router is invoked once per speculation round and selects,
+    per sequence and step, which drafter's candidates are verified.  Sequence b
+    owns packed rows [offsets[b], offsets[b+1]).  choice 0 (DFlash) needs K+1
+    rows, choice 1 (EAGLE-3) needs N rows; any other combination, or offsets
+    outside [0, total_rows] or decreasing, is malformed: AL = 0, bonus = -1,
+    best_node = -1.  For chain sequences best_node is the index of the last
+    accepted chain position (AL - 1).
+    Returns (AL, bonus, best_node) int32 [B].
+    """
+    t_rows = np.asarray(t_rows)
+    total = t_rows.shape[0]
+    B = len(choice)
+    al = np.full(B, MALFORMED_AL, np.int32)
+    bonus = np.full(B, MALFORMED_BONUS, np.int32)
+    best = np.full(B, -1, np.int32)
+    for b in range(B):
+        lo, hi, c = int(offsets[b]), int(offsets[b + 1]), int(choice[b])
+        if not (0 <= lo <= hi <= total):
+            continue
+        if c == 0 and hi - lo == K + 1:
+            a, bo = verify_chain(t_rows[lo:hi][None, :], np.asarray(chain_draft[b])[None, :K])
+            al[b], bonus[b], best[b] = a[0], bo[0], a[0] - 1
+        elif c == 1 and hi - lo == N:
+            a, bo, be = verify_tree(t_rows[lo:hi][None, :], np.asarray(parent[b])[None, :],
+                                    np.asarray(draft_ids[b])[None, :], d2t, V)
+            al[b], bonus[b], best[b] = a[0], bo[0], be[0]
+    return al, bonus, best
