@@ -1,0 +1,330 @@
+"""Benchmark of the per-round WhiFlash verify-and-route step on one MI355X.
+
+One step = one speculation round over a batch: the neural router
+(whiflash_route) followed by greedy verification of that batch's candidates
+(whiflash_verify_routed: argmax sweep over every logits row, d2t remap,
+chain / tree acceptance, emission), on one HIP stream.
+
+Workloads:
+  routed (default): 128 sequences, bf16 hidden [128, 2560] through the router
+      (2560 -> 1024 -> 1, threshold 1.0, exact 64/64 split); 64 DFlash chains of
+      K = 16 (17 rows) and 64 EAGLE-3 trees of 61 nodes, packed into 4,992 bf16
+      logits rows of 151,936 (1.517 GB per round).
+  sweep: 256 DFlash chains, K = 16, bf16 logits [256, 17, 151936] (1.32 GB per
+      round) plus the router on bf16 hidden [256, 2560]; a pool of distinct
+      seeded rounds resident in HBM is cycled so every step reads fresh logits.
+
+Prints one JSON line (rounds/s, logits GB/s, roofline of the argmax sweep and
+the CPU oracle baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "argmax_sweep_traffic.json")
+SWEEP_SRC = os.path.join(ROOT, "drafter_routing_verification_amd", "csrc", "sweep.hip")
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", choices=["routed", "sweep"], default="routed")
+    p.add_argument("--pool", type=int, default=4, help="distinct rounds resident in HBM (sweep)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def _to_dev(a, torch, dev):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+def _sweep_source_hash() -> str:
+    with open(SWEEP_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(workload: str, launches_bytes: float):
+    """HBM bytes per sweep launch from the committed counter summary, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("sweep_source_sha256_16") != _sweep_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- workloads
+
+
+class Routed:
+    name = "routed_bf16"
+
+    def __init__(self, torch, dev):
+        from synth import make_config
+        import drafter_routing_verification_amd as wf
+        t0 = time.time()
+        batch, r = make_config(3)
+        self.batch, self.router = batch, r
+        self.V, self.rows, self.B = batch.V, batch.rows, batch.B
+        T = lambda a: _to_dev(a, torch, dev)
+        self.hidden, self.W1, self.W2 = T(r.hidden), T(r.W1), T(r.W2)
+        self.b1 = T(r.b1)
+        self.b2 = torch.tensor([r.b2], dtype=torch.float32, device=dev)
+        self.logits = T(batch.logits)
+        self.offsets, self.chain_draft = T(batch.offsets), T(batch.chain_draft)
+        self.parent, self.draft_ids, self.d2t = T(batch.parent), T(batch.draft_ids), T(batch.d2t)
+        B = self.B
+        self.dal = torch.empty(B, dtype=torch.float32, device=dev)
+        self.choice = torch.empty(B, dtype=torch.int32, device=dev)
+        self.al = torch.empty(B, dtype=torch.int32, device=dev)
+        self.bonus = torch.empty(B, dtype=torch.int32, device=dev)
+        self.best = torch.empty(B, dtype=torch.int32, device=dev)
+        self.rws = torch.empty(wf.route_workspace_bytes(B, r.m), dtype=torch.uint8, device=dev)
+        self.vws = torch.empty(wf.verify_workspace_bytes(self.rows, self.V), dtype=torch.uint8,
+                               device=dev)
+        self.wf = wf
+        self.setup_s = time.time() - t0
+        esz = 2
+        self.logits_bytes = self.rows * self.V * esz
+        self.router_bytes = (r.hidden.size + r.W1.size + r.W2.size) * esz + r.b1.size * 4
+        meta = (batch.offsets.size + B * batch.K + 2 * B * batch.N + batch.d2t.size + 5 * B) * 4
+        self.step_bytes = self.logits_bytes + self.router_bytes + meta
+
+    def route(self, i):
+        r = self.router
+        self.wf.route(self.hidden, self.W1, self.b1, self.W2, self.b2, r.tau, delta_al=self.dal,
+                      choice=self.choice, workspace=self.rws)
+
+    def verify(self, i):
+        self.wf.verify_routed(self.logits, self.offsets, self.rows, self.choice, self.chain_draft,
+                              self.parent, self.draft_ids, self.d2t, row_argmax=False,
+                              accept_len=self.al, bonus=self.bonus, best_node=self.best,
+                              workspace=self.vws)
+
+    def check(self):
+        al = self.al.cpu().numpy()
+        ch = self.choice.cpu().numpy()
+        assert np.array_equal(ch, self.batch.layout_choice), "router choice differs from the layout"
+        assert al.min() >= 1, "a sequence came out malformed"
+        return float(al.mean())
+
+    def cpu_baseline(self, budget_s):
+        """The oracle on a bounded sample of this workload: the full router, and the argmax +
+        acceptance of whole sequences (chains and trees alternately) until the budget is spent."""
+        import oracle
+        from threadpoolctl import threadpool_limits
+        b, r = self.batch, self.router
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)
+            t_route = time.perf_counter() - t0
+            rows_done, seqs, t_verify = 0, 0, 0.0
+            chains = [s for s in range(b.B) if b.layout_choice[s] == 0]
+            trees = [s for s in range(b.B) if b.layout_choice[s] == 1]
+            order = [x for pair in zip(chains, trees) for x in pair]
+            while t_verify < budget_s and seqs < len(order):
+                s = order[seqs]
+                lo, hi = int(b.offsets[s]), int(b.offsets[s + 1])
+                t0 = time.perf_counter()
+                t = oracle.row_argmax(b.logits[lo:hi], b.dtype)
+                if b.layout_choice[s] == 0:
+                    oracle.verify_chain(t[None], b.chain_draft[s][None])
+                else:
+                    oracle.verify_tree(t[None], b.parent[s][None], b.draft_ids[s][None], b.d2t, b.V)
+                t_verify += time.perf_counter() - t0
+                rows_done += hi - lo
+                seqs += 1
+        per_round = t_route + t_verify * self.rows / rows_done
+        return {"value": 1.0 / per_round, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+                "sample": f"full router (B={b.B}) + argmax/acceptance of {seqs} whole sequences "
+                          f"({rows_done} of {self.rows} rows, alternating chain/tree), "
+                          f"scaled to {self.rows} rows; {t_route + t_verify:.1f} s of CPU work",
+                "seconds_per_round": per_round}
+
+
+class Sweep:
+    name = "sweep_bf16"
+
+    def __init__(self, torch, dev, pool):
+        from synth import make_chain_batch, make_router_inputs
+        from synth.workloads import CONFIGS, V_QWEN3, PLANT_BOOST
+        import drafter_routing_verification_amd as wf
+        t0 = time.time()
+        c = CONFIGS[4]
+        self.B, self.K, self.V = c["B"], c["K"], V_QWEN3
+        self.rows = self.B * (self.K + 1)
+        self.pool = []
+        g = torch.Generator(device=dev)
+        for rnd in range(pool):
+            cb = make_chain_batch(c["seed"], self.B, self.K, self.V, "bf16", 0.8, rnd, logits=False)
+            r = make_router_inputs(c["seed"], self.B, dtype="bf16", rnd=rnd)
+            g.manual_seed(c["seed"] * 1_000_003 + rnd)
+            x = torch.randn((self.rows, self.V), generator=g, device=dev, dtype=torch.float32)
+            planted = torch.from_numpy(cb.planted.reshape(-1).astype(np.int64)).to(dev)
+            x[torch.arange(self.rows, device=dev), planted] += PLANT_BOOST
+            logits = x.to(torch.bfloat16)
+            del x
+            self.pool.append(dict(logits=logits, draft=_to_dev(cb.draft, torch, dev),
+                                  hidden=_to_dev(r.hidden, torch, dev)))
+            if rnd == 0:
+                self.W1, self.W2 = _to_dev(r.W1, torch, dev), _to_dev(r.W2, torch, dev)
+                self.b1 = _to_dev(r.b1, torch, dev)
+                self.m, self.tau = r.m, r.tau
+                self.router_bytes = (r.hidden.size + r.W1.size + r.W2.size) * 2 + r.b1.size * 4
+        self.dal = torch.empty(self.B, dtype=torch.float32, device=dev)
+        self.choice = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.al = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.bonus = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.rws = torch.empty(wf.route_workspace_bytes(self.B, self.m), dtype=torch.uint8, device=dev)
+        self.vws = torch.empty(wf.verify_workspace_bytes(self.rows, self.V), dtype=torch.uint8,
+                               device=dev)
+        self.wf = wf
+        self.setup_s = time.time() - t0
+        self.logits_bytes = self.rows * self.V * 2
+        self.step_bytes = self.logits_bytes + self.router_bytes + (self.B * self.K + 4 * self.B) * 4
+
+    def route(self, i):
+        p = self.pool[i % len(self.pool)]
+        self.wf.route(p["hidden"], self.W1, self.b1, self.W2, None, self.tau, delta_al=self.dal,
+                      choice=self.choice, workspace=self.rws)
+
+    def verify(self, i):
+        p = self.pool[i % len(self.pool)]
+        self.wf.verify_chain(p["logits"], p["draft"], row_argmax=False, accept_len=self.al,
+                             bonus=self.bonus, workspace=self.vws)
+
+    def check(self):
+        al = self.al.cpu().numpy()
+        assert al.min() >= 1 and al.max() <= self.K + 1
+        return float(al.mean())
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        from threadpoolctl import threadpool_limits
+        p = self.pool[0]
+        raw = p["logits"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+        draft = p["draft"].cpu().numpy()
+        R = self.K + 1
+        with threadpool_limits(limits=1):
+            seqs, t_verify = 0, 0.0
+            while t_verify < budget_s and seqs < self.B:
+                t0 = time.perf_counter()
+                t = oracle.row_argmax(raw[seqs * R:(seqs + 1) * R], "bf16")
+                oracle.verify_chain(t[None], draft[seqs][None])
+                t_verify += time.perf_counter() - t0
+                seqs += 1
+        per_round = t_verify * self.B / seqs
+        return {"value": 1.0 / per_round, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+                "sample": f"argmax + chain acceptance of {seqs} of {self.B} sequences, scaled to "
+                          f"the batch (router excluded); {t_verify:.1f} s of CPU work",
+                "seconds_per_round": per_round}
+
+
+# ----------------------------------------------------------------------------- main
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (sequences are "
+              "independent, so N GPUs would each run this step on B/N sequences)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    work = Routed(torch, dev) if args.workload == "routed" else Sweep(torch, dev, args.pool)
+    stream = torch.cuda.current_stream()
+    print(f"# workload {work.name}: inputs resident in HBM ({work.setup_s:.1f} s setup)",
+          file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        work.route(i)
+        work.verify(i)
+    torch.cuda.synchronize()
+    mean_al = work.check()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        work.route(i)
+        ev[i][1].record(stream)
+        work.verify(i)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_total_ms = ev[0][0].elapsed_time(ev[K - 1][2])
+    route_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    verify_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    work.check()
+
+    ms_per_step = gpu_total_ms / K
+    rounds_per_s = 1000.0 / ms_per_step
+    verify_s = float(verify_ms.mean()) / 1000.0
+    achieved = work.logits_bytes / verify_s / 1e9
+    traffic = _traffic(work.name, work.logits_bytes)
+    out = {
+        "metric": "verify+route rounds/s (1 GPU); logits HBM GB/s of the verify sweep",
+        "value": round(rounds_per_s, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; planted-argmax logits, random trees, random router weights)",
+        "config": {"workload": work.name, "batch": work.B, "logits_rows": work.rows,
+                   "vocab": work.V, "hidden": 2560, "router_width": 1024,
+                   "logits_bytes_per_round": work.logits_bytes,
+                   "bytes_per_round": work.step_bytes},
+        "logits_GBps": round(achieved, 1),
+        "route_us_median": round(float(np.median(route_ms)) * 1000, 2),
+        "verify_us_median": round(float(np.median(verify_ms)) * 1000, 2),
+        "verify_us_p10_p90": [round(float(np.percentile(verify_ms, q)) * 1000, 2) for q in (10, 90)],
+        "wall_ms_per_step": round(wall * 1000 / K, 5),
+        "mean_accept_len": round(mean_al, 3),
+        "roofline": {
+            "kernel": "argmax sweep + acceptance (one whiflash_verify_* call)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        base = work.cpu_baseline(args.cpu_seconds)
+        base.pop("seconds_per_round", None)
+        out["cpu_baseline"] = base
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

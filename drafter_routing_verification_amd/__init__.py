@@ -1,0 +1,34 @@
+"""Python binding of libwhiflash, the MI355X verify-and-route library.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in ``include/whiflash.h``.  Tensors must be torch device tensors on a
+ROCm GPU; outputs are allocated here when not supplied.  There is no CPU
+fallback: if the shared library is missing the import of the binding fails.
+
+Entry points (same names as the C ABI):
+    route(hidden, W1, b1, W2, b2, tau)                    -> (delta_al, choice)
+    verify_chain(logits, draft)                           -> (accept_len, bonus, row_argmax)
+    verify_tree(logits, parent, draft_ids, d2t)           -> (accept_len, bonus, best_node, row_argmax)
+    verify_routed(logits, row_offsets, total_rows, choice, chain_draft, parent, draft_ids, d2t)
+                                                          -> (accept_len, bonus, best_node, row_argmax)
+"""
+
+from ._binding import (  # noqa: F401
+    WF_F32,
+    WF_BF16,
+    WF_OK,
+    WhiflashError,
+    lib,
+    library_path,
+    status_string,
+    route_workspace_bytes,
+    verify_workspace_bytes,
+    route,
+    verify_chain,
+    verify_tree,
+    verify_routed,
+    whiflash_route,
+    whiflash_verify_chain,
+    whiflash_verify_tree,
+    whiflash_verify_routed,
+)

@@ -1,0 +1,166 @@
+// C ABI of libwhiflash: host-side validation, workspace carving and launches.
+// Every check here runs before any HIP call, so a rejected call launches
+// nothing and touches no device state.
+#include <stdint.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr size_t kWorkspaceAlign = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+inline int32_t elem_bytes(int32_t dtype) { return dtype == WF_BF16 ? 2 : 4; }
+
+inline bool valid_dtype(int32_t dtype) { return dtype == WF_F32 || dtype == WF_BF16; }
+
+int32_t check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return WF_OK;
+  if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kWorkspaceAlign != 0 || have < need)
+    return WF_ERR_WORKSPACE;
+  return WF_OK;
+}
+
+// Shared checks of the logits operand.
+int32_t check_logits(const void* logits, int32_t dtype, int32_t rows, int32_t V, int64_t row_stride) {
+  if (!valid_dtype(dtype)) return WF_ERR_DTYPE;
+  if (V <= 0 || rows < 0 || row_stride < V) return WF_ERR_SHAPE;
+  if (rows > 0 && logits == nullptr) return WF_ERR_NULL;
+  if (!aligned16(logits) || (row_stride * elem_bytes(dtype)) % 16 != 0) return WF_ERR_ALIGN;
+  const wf::SweepPlan plan = wf::sweep_plan(rows, V);
+  // 1-D grid of 256-thread workgroups: keep the work-item count below 2^32.
+  if (static_cast<int64_t>(rows) * plan.splits * wf::kThreads >= (int64_t{1} << 32))
+    return WF_ERR_SHAPE;
+  return WF_OK;
+}
+
+int32_t launch_status(hipError_t e) { return e == hipSuccess ? WF_OK : WF_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* whiflash_status_string(int32_t status) {
+  switch (status) {
+    case WF_OK: return "WF_OK";
+    case WF_ERR_NULL: return "WF_ERR_NULL: a required pointer is NULL";
+    case WF_ERR_SHAPE: return "WF_ERR_SHAPE: a size is out of range";
+    case WF_ERR_DTYPE: return "WF_ERR_DTYPE: unknown element type";
+    case WF_ERR_ALIGN: return "WF_ERR_ALIGN: logits base or row stride not 16-byte aligned";
+    case WF_ERR_WORKSPACE: return "WF_ERR_WORKSPACE: workspace NULL, not 256-byte aligned, or too small";
+    case WF_ERR_LAUNCH: return "WF_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown whiflash status";
+  }
+}
+
+size_t whiflash_route_workspace_bytes(int32_t B, int32_t m) {
+  if (B <= 0 || m <= 0) return 0;
+  // The GEMV path needs B * m partials; the MFMA path fewer.
+  return round_up(static_cast<size_t>(B) * static_cast<size_t>(m) * sizeof(float), kWorkspaceAlign);
+}
+
+size_t whiflash_verify_workspace_bytes(int32_t total_rows, int32_t V) {
+  if (total_rows <= 0 || V <= 0) return 0;
+  const wf::SweepPlan plan = wf::sweep_plan(total_rows, V);
+  return round_up(static_cast<size_t>(total_rows) * plan.splits * sizeof(wf::Partial), kWorkspaceAlign);
+}
+
+int32_t whiflash_route(const void* hidden, int32_t dtype, int32_t B, int32_t d, const void* W1,
+                       const float* b1, int32_t m, const void* W2, const float* b2, float tau,
+                       float* delta_al, int32_t* choice, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  if (!valid_dtype(dtype)) return WF_ERR_DTYPE;
+  if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
+  if (B == 0) return WF_OK;
+  if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
+  if (static_cast<int64_t>(B) * m > INT32_MAX || static_cast<int64_t>(m) * d > (int64_t{1} << 40))
+    return WF_ERR_SHAPE;
+  const int32_t s = check_workspace(workspace, workspace_bytes, whiflash_route_workspace_bytes(B, m));
+  if (s != WF_OK) return s;
+  float* part = static_cast<float*>(workspace);
+  const bool mfma = wf::router_use_mfma(dtype, B, d, hidden, W1);
+  const int32_t P = wf::router_partials(B, m, mfma);
+  hipError_t e = mfma ? wf::launch_router_mfma(hidden, B, d, W1, b1, m, W2, part, stream)
+                      : wf::launch_router_gemv(hidden, dtype, B, d, W1, b1, m, W2, part, stream);
+  if (e != hipSuccess) return WF_ERR_LAUNCH;
+  return launch_status(wf::launch_router_reduce(part, P, B, b2, tau, delta_al, choice, stream));
+}
+
+int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int32_t K, int32_t V,
+                              int64_t row_stride, const int32_t* draft, int32_t* accept_len,
+                              int32_t* bonus, int32_t* row_argmax, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
+  const int64_t rows64 = static_cast<int64_t>(B) * (K + 1);
+  if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
+  const int32_t rows = static_cast<int32_t>(rows64);
+  int32_t s = check_logits(logits, dtype, rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!accept_len || !bonus || (K > 0 && !draft)) return WF_ERR_NULL;
+  const size_t need = whiflash_verify_workspace_bytes(rows, V);
+  if ((s = check_workspace(workspace, workspace_bytes, need)) != WF_OK) return s;
+  const wf::SweepPlan plan = wf::sweep_plan(rows, V);
+  wf::Partial* part = static_cast<wf::Partial*>(workspace);
+  if (wf::launch_sweep(logits, dtype, row_stride, rows, V, plan, part, stream) != hipSuccess)
+    return WF_ERR_LAUNCH;
+  return launch_status(wf::launch_finalize_chain(part, plan.splits, B, K, draft, accept_len, bonus,
+                                                 row_argmax, stream));
+}
+
+int32_t whiflash_verify_tree(const void* logits, int32_t dtype, int32_t B, int32_t N, int32_t V,
+                             int64_t row_stride, const int32_t* parent, const int32_t* draft_ids,
+                             const int32_t* d2t, int32_t Vd, int32_t* accept_len, int32_t* bonus,
+                             int32_t* best_node, int32_t* row_argmax, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || N < 1 || N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1) return WF_ERR_SHAPE;
+  const int64_t rows64 = static_cast<int64_t>(B) * N;
+  if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
+  const int32_t rows = static_cast<int32_t>(rows64);
+  int32_t s = check_logits(logits, dtype, rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!parent || !draft_ids || !d2t || !accept_len || !bonus) return WF_ERR_NULL;
+  const size_t need = whiflash_verify_workspace_bytes(rows, V);
+  if ((s = check_workspace(workspace, workspace_bytes, need)) != WF_OK) return s;
+  const wf::SweepPlan plan = wf::sweep_plan(rows, V);
+  wf::Partial* part = static_cast<wf::Partial*>(workspace);
+  if (wf::launch_sweep(logits, dtype, row_stride, rows, V, plan, part, stream) != hipSuccess)
+    return WF_ERR_LAUNCH;
+  return launch_status(wf::launch_finalize_tree(part, plan.splits, B, N, V, parent, draft_ids, d2t,
+                                                Vd, accept_len, bonus, best_node, row_argmax,
+                                                stream));
+}
+
+int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int32_t V,
+                               int64_t row_stride, const int32_t* row_offsets, int32_t total_rows,
+                               const int32_t* choice, int32_t K, const int32_t* chain_draft,
+                               int32_t N, const int32_t* parent, const int32_t* draft_ids,
+                               const int32_t* d2t, int32_t Vd, int32_t* accept_len, int32_t* bonus,
+                               int32_t* best_node, int32_t* row_argmax, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+      N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
+    return WF_ERR_SHAPE;
+  int32_t s = check_logits(logits, dtype, total_rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!row_offsets || !choice || (K > 0 && !chain_draft) || !parent || !draft_ids || !d2t ||
+      !accept_len || !bonus)
+    return WF_ERR_NULL;
+  const size_t need = whiflash_verify_workspace_bytes(total_rows, V);
+  if ((s = check_workspace(workspace, workspace_bytes, need)) != WF_OK) return s;
+  const wf::SweepPlan plan = wf::sweep_plan(total_rows, V);
+  wf::Partial* part = static_cast<wf::Partial*>(workspace);
+  if (wf::launch_sweep(logits, dtype, row_stride, total_rows, V, plan, part, stream) != hipSuccess)
+    return WF_ERR_LAUNCH;
+  return launch_status(wf::launch_finalize_routed(part, plan.splits, B, V, row_offsets, total_rows,
+                                                  choice, K, chain_draft, N, parent, draft_ids, d2t,
+                                                  Vd, accept_len, bonus, best_node, row_argmax,
+                                                  stream));
+}
+
+}  // extern "C"

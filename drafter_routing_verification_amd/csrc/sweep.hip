@@ -1,0 +1,202 @@
+// Full-vocabulary argmax sweep over target logits rows (greedy verification:
+// the target's token at each drafted position is the lowest index holding the
+// row maximum; WhiFlash paper, section 3.2, with greedy decoding).
+//
+// HBM-bound streaming kernel.  Each workgroup owns one chunk of one row and
+// reads it once with 16-byte loads, 256 threads side by side so every wave64
+// load instruction covers 1 KiB of contiguous memory.  A thread keeps its
+// running maximum and the 16-byte vector where it first reached it (strict
+// ">" in increasing index order keeps the earliest), and only at the end
+// re-reads that one vector to recover the element index.  The per-chunk
+// (max, index) pair is reduced across the wave with cross-lane shuffles and
+// across the four waves in LDS; ties go to the lower index at every level.
+#include <math.h>
+
+#include "common.h"
+
+namespace wf {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kUnroll = 8;  // 16-byte loads in flight per thread
+
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<WF_BF16> {
+  static constexpr int kPerVec = 8;
+  static constexpr int kBytes = 2;
+  // bfloat16 is the high half of a binary32 word: widening is exact.
+  __device__ static inline float lo(unsigned w) { return __uint_as_float(w << 16); }
+  __device__ static inline float hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static inline float vmax(u32x4 v) {
+    float a = fmaxf(fmaxf(lo(v.x), hi(v.x)), lo(v.y));
+    float b = fmaxf(fmaxf(hi(v.y), lo(v.z)), hi(v.z));
+    float c = fmaxf(fmaxf(lo(v.w), hi(v.w)), a);
+    return fmaxf(b, c);
+  }
+  // First element of the vector equal to `m` (0 if none, e.g. NaN input).
+  __device__ static inline int first_equal(u32x4 v, float m) {
+    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+    int j = 0;
+#pragma unroll
+    for (int k = 7; k >= 0; --k) {
+      const float x = (k & 1) ? hi(w[k >> 1]) : lo(w[k >> 1]);
+      if (x == m) j = k;
+    }
+    return j;
+  }
+  __device__ static inline float scalar(const unsigned char* row, int e) {
+    const unsigned short b = reinterpret_cast<const unsigned short*>(row)[e];
+    return __uint_as_float(static_cast<unsigned>(b) << 16);
+  }
+};
+
+template <>
+struct Elem<WF_F32> {
+  static constexpr int kPerVec = 4;
+  static constexpr int kBytes = 4;
+  __device__ static inline float vmax(u32x4 v) {
+    return fmaxf(fmaxf(__uint_as_float(v.x), __uint_as_float(v.y)),
+                 fmaxf(__uint_as_float(v.z), __uint_as_float(v.w)));
+  }
+  __device__ static inline int first_equal(u32x4 v, float m) {
+    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+    int j = 0;
+#pragma unroll
+    for (int k = 3; k >= 0; --k)
+      if (__uint_as_float(w[k]) == m) j = k;
+    return j;
+  }
+  __device__ static inline float scalar(const unsigned char* row, int e) {
+    return reinterpret_cast<const float*>(row)[e];
+  }
+};
+
+// (v, i) beats (bv, bi) when larger, or equal with a lower index.
+__device__ inline void take_better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+__device__ inline u32x4 load16(const u32x4* p) { return __builtin_nontemporal_load(p); }
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void argmax_sweep_kernel(
+    const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
+    int chunk_vecs, int nvec, Partial* __restrict__ part) {
+  using E = Elem<DT>;
+  const int blk = blockIdx.x;
+  const int row = blk / splits;
+  const int c = blk - row * splits;
+  const unsigned char* rowp = logits + static_cast<int64_t>(row) * row_bytes;
+  const u32x4* vp = reinterpret_cast<const u32x4*>(rowp);
+  const int tid = threadIdx.x;
+  const int v0 = c * chunk_vecs;
+  const int v1 = min(v0 + chunk_vecs, nvec);
+
+  float best = -INFINITY;
+  int bestv = v0 + tid;  // vector where `best` was first reached
+  int v = v0 + tid;
+  for (; v + (kUnroll - 1) * kThreads < v1; v += kUnroll * kThreads) {
+    u32x4 d[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) d[u] = load16(vp + v + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float m = E::vmax(d[u]);
+      if (m > best) {
+        best = m;
+        bestv = v + u * kThreads;
+      }
+    }
+  }
+  for (; v < v1; v += kThreads) {
+    const float m = E::vmax(load16(vp + v));
+    if (m > best) {
+      best = m;
+      bestv = v;
+    }
+  }
+
+  int idx = INT_MAX;
+  if (v0 + tid < v1) {
+    idx = bestv * E::kPerVec + E::first_equal(vp[bestv], best);
+  } else {
+    best = -INFINITY;
+  }
+  // Elements past the last full vector (V not a multiple of the vector width).
+  if (c == splits - 1 && tid == 0) {
+    for (int e = nvec * E::kPerVec; e < V; ++e) {
+      const float x = E::scalar(rowp, e);
+      if (x > best || idx == INT_MAX) {
+        best = x;
+        idx = e;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(best, off);
+    const int oi = __shfl_xor(idx, off);
+    take_better(best, idx, ov, oi);
+  }
+  __shared__ float sv[kWaves];
+  __shared__ int si[kWaves];
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = idx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float bv = sv[0];
+    int bi = si[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) take_better(bv, bi, sv[w], si[w]);
+    part[blk] = Partial{bv, bi};
+  }
+}
+
+}  // namespace
+
+SweepPlan sweep_plan(int32_t rows, int32_t V) {
+  // Aim for enough workgroups to keep all 256 CUs streaming with a short
+  // tail, but keep every chunk at least 2048 elements long.
+  constexpr int64_t kTargetBlocks = 8192;
+  constexpr int64_t kMinChunk = 2048;
+  const int64_t max_splits = V / kMinChunk > 1 ? V / kMinChunk : 1;
+  int64_t splits = (kTargetBlocks + rows - 1) / (rows > 0 ? rows : 1);
+  if (splits < 1) splits = 1;
+  if (splits > max_splits) splits = max_splits;
+  int64_t chunk = (V + splits - 1) / splits;
+  chunk = (chunk + 7) / 8 * 8;
+  splits = (V + chunk - 1) / chunk;
+  return SweepPlan{static_cast<int32_t>(splits), static_cast<int32_t>(chunk)};
+}
+
+hipError_t launch_sweep(const void* logits, int dtype, int64_t row_stride, int32_t rows, int32_t V,
+                        SweepPlan plan, Partial* part, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(rows) * plan.splits;
+  if (blocks == 0) return hipSuccess;
+  const unsigned char* base = static_cast<const unsigned char*>(logits);
+  if (dtype == WF_BF16) {
+    using E = Elem<WF_BF16>;
+    hipLaunchKernelGGL(argmax_sweep_kernel<WF_BF16>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, base, row_stride * E::kBytes, V, plan.splits,
+                       plan.chunk / E::kPerVec, V / E::kPerVec, part);
+  } else {
+    using E = Elem<WF_F32>;
+    hipLaunchKernelGGL(argmax_sweep_kernel<WF_F32>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, base, row_stride * E::kBytes, V, plan.splits,
+                       plan.chunk / E::kPerVec, V / E::kPerVec, part);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace wf

@@ -1,0 +1,176 @@
+/*
+ * whiflash.h -- C ABI of the MI355X (gfx950) verify-and-route library.
+ *
+ * One WhiFlash speculation round ends with three steps, all implemented here
+ * as HIP kernels:
+ *   route  : the neural router, a two-layer GELU MLP mapping the target's
+ *            final hidden state to a predicted acceptance-length gain, and the
+ *            hardware-aware threshold that turns it into a drafter choice;
+ *   verify : greedy verification -- a full-vocabulary argmax of the target
+ *            logits at every drafted position, then the accepted prefix of a
+ *            DFlash block (chain) or the deepest accepted path of an EAGLE-3
+ *            draft tree (after mapping draft-vocabulary ids to target ids);
+ *   emit   : acceptance length (AL) and bonus token per sequence.
+ * Sources: "WhiFlash: Accelerating Speculative Decoding with Token-Level
+ * Cross-Paradigm Routing" (arXiv 2606.07710), sections 3.2 and 3.3 and
+ * Appendix A; the "Qwen3-4B-EAGLE3" model card (fixed 32K draft vocabulary).
+ *
+ * Conventions shared by every entry point:
+ *   - Every array argument is a DEVICE pointer owned by the caller.  The
+ *     library keeps no pointer after the call returns and holds no state.
+ *   - Calls are asynchronous on `stream` (0 = the default stream); none
+ *     synchronises and none allocates.  Scratch memory comes from the
+ *     caller's `workspace` (device memory of at least the size returned by
+ *     the matching *_workspace_bytes function, 256-byte aligned).  Calls on
+ *     different streams must use different workspaces.
+ *   - Arrays are row-major.  Logits rows are `row_stride` elements apart;
+ *     row_stride >= V, and the logits base address and row_stride * element
+ *     size must both be multiples of 16 bytes.
+ *   - Return value: WF_OK, or a negative wf_status for a problem the host
+ *     can see (null pointer, bad size, dtype, alignment, workspace too
+ *     small); nothing is launched then.  WF_ERR_LAUNCH reports a failed
+ *     kernel launch.
+ *   - Bad DATA never faults and has a defined result (identical in the CPU
+ *     oracle): see each entry point.  Logits must not be NaN (the argmax of a
+ *     row holding NaN is unspecified, but still an index in [0, V)).
+ */
+#ifndef WHIFLASH_H
+#define WHIFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of logits, hidden states and router weights. */
+typedef enum { WF_F32 = 0, WF_BF16 = 1 } wf_dtype;
+
+typedef enum {
+  WF_OK = 0,
+  WF_ERR_NULL = -1,      /* a required pointer is NULL                       */
+  WF_ERR_SHAPE = -2,     /* a size is out of range                           */
+  WF_ERR_DTYPE = -3,     /* dtype is not a wf_dtype value                    */
+  WF_ERR_ALIGN = -4,     /* logits base or row stride not 16-byte aligned    */
+  WF_ERR_WORKSPACE = -5, /* workspace NULL, misaligned or smaller than needed */
+  WF_ERR_LAUNCH = -6     /* the HIP runtime rejected a kernel launch         */
+} wf_status;
+
+/* Largest K+1 (chain) or N (tree) rows per sequence the kernels accept. */
+#define WHIFLASH_MAX_SEQ_ROWS 1024
+
+/* Human-readable name of a wf_status value (static string; host only). */
+const char* whiflash_status_string(int32_t status);
+
+/* Workspace bytes whiflash_route needs for batch B and router width m.
+ * Returns 0 when B or m is not positive. Host only. */
+size_t whiflash_route_workspace_bytes(int32_t B, int32_t m);
+
+/* Workspace bytes the verify entry points need for `total_rows` logits rows
+ * of V entries (chain: B*(K+1) rows, tree: B*N rows, routed: total_rows).
+ * Returns 0 when total_rows or V is not positive. Host only. */
+size_t whiflash_verify_workspace_bytes(int32_t total_rows, int32_t V);
+
+/*
+ * Neural router + hardware-aware threshold (WhiFlash paper, section 3.3.2
+ * "Neural Policy" and "Hardware-Aware Routing Decision"; Appendix A "Neural
+ * Router Architecture"):
+ *     z        = W1 h_b + b1                       (d -> m)
+ *     g        = GELU(z) = z/2 * (1 + erf(z/sqrt 2)), dropout = identity
+ *     dal[b]   = W2 . g + b2                       (m -> 1, predicted AL gain)
+ *     choice[b]= 1 (EAGLE-3, autoregressive tree) if dal[b] > tau, else 0 (DFlash)
+ *   hidden [B, d], W1 [m, d], W2 [m]: all of element type `dtype`.
+ *   b1 [m] float32 or NULL (= 0); b2: pointer to one float32 or NULL (= 0).
+ *   Accumulation, GELU and the second layer run in float32.
+ *   delta_al [B] float32 and choice [B] int32 are written.
+ * B == 0 is a no-op. d, m >= 1.  The paper's router uses m = d/8; any m works.
+ */
+int32_t whiflash_route(const void* hidden, int32_t dtype, int32_t B, int32_t d,
+                       const void* W1, const float* b1, int32_t m,
+                       const void* W2, const float* b2, float tau,
+                       float* delta_al, int32_t* choice,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy verification of DFlash blocks (WhiFlash paper, section 3.2: the
+ * drafted block is verified in parallel and decoding continues from the last
+ * accepted token; section 4 "Metrics": AL counts tokens per round).
+ *   logits: B*(K+1) rows; row b*(K+1)+i is the target's prediction after the
+ *           first i draft tokens of sequence b (row K follows a full match).
+ *   draft [B, K] int32 target ids.
+ *   t[r] = lowest index holding the maximum of row r.
+ *   n = first i < K with draft[b,i] != t[b*(K+1)+i], else K;
+ *   accept_len[b] = n + 1 (in [1, K+1]); bonus[b] = t[b*(K+1)+n].
+ *   row_argmax [B*(K+1)] (t) is written when not NULL.
+ * A draft id outside [0, V) never matches.  B == 0 is a no-op; K >= 0;
+ * K + 1 <= WHIFLASH_MAX_SEQ_ROWS.
+ */
+int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int32_t K, int32_t V,
+                              int64_t row_stride, const int32_t* draft,
+                              int32_t* accept_len, int32_t* bonus, int32_t* row_argmax,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy verification of EAGLE-3 draft trees with the draft-to-target map
+ * (WhiFlash paper, section 3.2: a tree of candidate tokens is verified;
+ * "Qwen3-4B-EAGLE3" card: draft ids come from a fixed 32K vocabulary).
+ *   logits: B*N rows; row b*N+u is the target's prediction after node u of
+ *           tree b.  Node 0 is the root (the last verified token).
+ *   parent [B, N] int32: parent[b,0] is ignored; node u >= 1 hangs under
+ *           parent[b,u], which must lie in [0, u) (else u is unreachable).
+ *   draft_ids [B, N] int32 draft-vocabulary ids (entry 0 ignored).
+ *   d2t [Vd] int32 absolute target id of each draft id.
+ *   Node u >= 1 is accepted iff its parent p is accepted and
+ *   d2t[draft_ids[b,u]] == t[b*N+p]; ids outside [0, Vd) and table entries
+ *   outside [0, V) never match.  best = deepest accepted node (lowest index
+ *   among equally deep ones); accept_len[b] = depth(best) + 1,
+ *   bonus[b] = t[b*N+best], best_node[b] = best (when not NULL).
+ *   row_argmax [B*N] is written when not NULL.
+ * B == 0 is a no-op; 1 <= N <= WHIFLASH_MAX_SEQ_ROWS; Vd >= 1.
+ */
+int32_t whiflash_verify_tree(const void* logits, int32_t dtype, int32_t B, int32_t N, int32_t V,
+                             int64_t row_stride, const int32_t* parent, const int32_t* draft_ids,
+                             const int32_t* d2t, int32_t Vd,
+                             int32_t* accept_len, int32_t* bonus, int32_t* best_node,
+                             int32_t* row_argmax,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Routed mixed batch: each sequence is verified by the drafter its router
+ * choice selected (WhiFlash paper, section 3.3: one routing decision per
+ * sequence and speculation round).
+ *   logits: total_rows packed rows; sequence b owns rows
+ *           [row_offsets[b], row_offsets[b+1]).
+ *   row_offsets [B+1] int32 (device); total_rows is the host's copy of the
+ *           number of packed rows (the sweep covers rows [0, total_rows)).
+ *   choice [B] int32 (e.g. the output of whiflash_route): 0 = DFlash chain
+ *           needing K+1 rows, verified with chain_draft[b, 0..K-1];
+ *           1 = EAGLE-3 tree needing N rows, verified with parent[b,:],
+ *           draft_ids[b,:] and d2t as in whiflash_verify_tree.
+ *   chain_draft [B, K], parent [B, N], draft_ids [B, N]: rows belonging to
+ *           sequences of the other kind are not read.
+ *   A sequence whose offsets are decreasing or outside [0, total_rows],
+ *   whose row count does not match its choice, or whose choice is neither 0
+ *   nor 1 gets accept_len 0, bonus -1, best_node -1 (AL 0 cannot occur
+ *   otherwise).  For chain sequences best_node = accept_len - 1.
+ *   row_argmax [total_rows] is written when not NULL, for every row covered
+ *   by some sequence's offsets range.
+ * B == 0 is a no-op; total_rows >= 0; K >= 0; K+1 and N <= WHIFLASH_MAX_SEQ_ROWS.
+ */
+int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int32_t V,
+                               int64_t row_stride, const int32_t* row_offsets, int32_t total_rows,
+                               const int32_t* choice,
+                               int32_t K, const int32_t* chain_draft,
+                               int32_t N, const int32_t* parent, const int32_t* draft_ids,
+                               const int32_t* d2t, int32_t Vd,
+                               int32_t* accept_len, int32_t* bonus, int32_t* best_node,
+                               int32_t* row_argmax,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WHIFLASH_H */

@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol the header declares, sizes workspaces, and rejects bad arguments with the
+documented status codes before launching anything."""
+
+import os
+import re
+
+import pytest
+
+import drafter_routing_verification_amd as wf
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "whiflash.h")
+V = 151936
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(whiflash_\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert {"whiflash_route", "whiflash_verify_chain", "whiflash_verify_tree",
+            "whiflash_verify_routed"} <= set(names)
+    lib = wf.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(-6, 1):
+        s = wf.status_string(code)
+        assert s.startswith("WF_") and s != "unknown whiflash status"
+    assert wf.status_string(5) == "unknown whiflash status"
+
+
+def test_workspace_sizes():
+    assert wf.verify_workspace_bytes(0, V) == 0 and wf.verify_workspace_bytes(5, 0) == 0
+    assert wf.route_workspace_bytes(0, 1024) == 0
+    for rows in (1, 17, 544, 488, 4352, 4992):
+        n = wf.verify_workspace_bytes(rows, V)
+        assert n % 256 == 0 and n >= rows * 8
+    assert wf.route_workspace_bytes(256, 1024) >= 256 * 1024 * 4
+
+
+ALIGNED = 1 << 20   # a fake, suitably aligned device address: validation fails before it is used
+
+
+def test_verify_chain_validation():
+    f = wf.whiflash_verify_chain
+    # (logits, dtype, B, K, V, stride, draft, al, bonus, rows, ws, ws_bytes, stream)
+    assert f(None, 1, 1, 16, V, V, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 1 << 20, None) == -1
+    assert f(ALIGNED, 9, 1, 16, V, V, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 1 << 20, None) == -3
+    assert f(ALIGNED, 1, 1, -1, V, V, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 1 << 20, None) == -2
+    assert f(ALIGNED, 1, 1, 1024, V, V, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 1 << 20, None) == -2
+    assert f(ALIGNED, 1, 1, 16, V, V - 1, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 1 << 20, None) == -2
+    assert f(ALIGNED, 1, 1, 16, 101, 101, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 1 << 20, None) == -4
+    assert f(ALIGNED + 2, 1, 1, 16, V, V, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 1 << 20, None) == -4
+    assert f(ALIGNED, 1, 1, 16, V, V, None, ALIGNED, ALIGNED, None, ALIGNED, 1 << 20, None) == -1
+    assert f(ALIGNED, 1, 1, 16, V, V, ALIGNED, ALIGNED, ALIGNED, None, None, 1 << 20, None) == -5
+    assert f(ALIGNED, 1, 1, 16, V, V, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 16, None) == -5
+    assert f(ALIGNED, 1, 1, 16, V, V, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED + 16, 1 << 20, None) == -5
+    assert f(None, 1, 0, 16, V, V, None, None, None, None, None, 0, None) == 0   # B = 0: no-op
+
+
+def test_verify_tree_validation():
+    f = wf.whiflash_verify_tree
+    args = [ALIGNED, 1, 8, 61, V, V, ALIGNED, ALIGNED, ALIGNED, 32000, ALIGNED, ALIGNED, None, None,
+            ALIGNED, 1 << 20, None]
+    bad = list(args); bad[3] = 0
+    assert f(*bad) == -2
+    bad = list(args); bad[3] = 1025
+    assert f(*bad) == -2
+    bad = list(args); bad[9] = 0
+    assert f(*bad) == -2
+    bad = list(args); bad[8] = None
+    assert f(*bad) == -1
+    bad = list(args); bad[15] = 100
+    assert f(*bad) == -5
+
+
+def test_verify_routed_validation():
+    f = wf.whiflash_verify_routed
+    args = [ALIGNED, 1, 128, V, V, ALIGNED, 4992, ALIGNED, 16, ALIGNED, 61, ALIGNED, ALIGNED,
+            ALIGNED, 32000, ALIGNED, ALIGNED, None, None, ALIGNED, 1 << 20, None]
+    bad = list(args); bad[5] = None
+    assert f(*bad) == -1
+    bad = list(args); bad[6] = -1
+    assert f(*bad) == -2
+    bad = list(args); bad[20] = 8
+    assert f(*bad) == -5
+
+
+def test_route_validation():
+    f = wf.whiflash_route
+    # (hidden, dtype, B, d, W1, b1, m, W2, b2, tau, dal, choice, ws, ws_bytes, stream)
+    assert f(ALIGNED, 2, 4, 2560, ALIGNED, None, 1024, ALIGNED, None, 1.0, ALIGNED, ALIGNED, ALIGNED,
+             1 << 24, None) == -3
+    assert f(ALIGNED, 1, 4, 0, ALIGNED, None, 1024, ALIGNED, None, 1.0, ALIGNED, ALIGNED, ALIGNED,
+             1 << 24, None) == -2
+    assert f(None, 1, 4, 2560, ALIGNED, None, 1024, ALIGNED, None, 1.0, ALIGNED, ALIGNED, ALIGNED,
+             1 << 24, None) == -1
+    assert f(ALIGNED, 1, 4, 2560, ALIGNED, None, 1024, ALIGNED, None, 1.0, ALIGNED, ALIGNED, ALIGNED,
+             64, None) == -5
+    assert f(None, 1, 0, 2560, None, None, 1024, None, None, 1.0, None, None, None, 0, None) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from drafter_routing_verification_amd import _binding
+    monkeypatch.setattr(_binding, "_LIB", None)
+    monkeypatch.setattr(_binding, "library_path", lambda: str(tmp_path / "libwhiflash.so"))
+    with pytest.raises(_binding.WhiflashError):
+        _binding.lib()

@@ -1,0 +1,95 @@
+"""GPU parity at the five workloads' full sizes, through the same entry points and
+launch configuration the benchmark times.  Every row argmax, acceptance length,
+bonus token, best node and routing choice is compared with the oracle bit for
+bit (choices except within 1e-3 of the threshold); Delta-AL within tolerance.
+Runs each workload twice to check the results are bitwise reproducible."""
+
+import numpy as np
+import pytest
+import torch
+
+import drafter_routing_verification_amd as wf
+import oracle
+from gpu_helpers import check_router, dev, host
+from synth import make_config
+from synth.workloads import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+
+def _route(r):
+    args = (dev(r.hidden), dev(r.W1), dev(r.b1), dev(r.W2), float(r.b2), r.tau)
+    out1 = [host(x) for x in wf.route(*args)]
+    out2 = [host(x) for x in wf.route(*args)]
+    assert np.array_equal(out1[0], out2[0]) and np.array_equal(out1[1], out2[1])
+    e_dal, e_ch = oracle.route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)
+    check_router(out1[0], out1[1], e_dal, e_ch, r.dtype, r.tau)
+    return out1[1], e_ch
+
+
+def _chain(idx, rnd=0):
+    print(f"workload {CONFIGS[idx]['name']} round {rnd}", flush=True)
+    batch, router = make_config(idx, rnd=rnd)
+    _route(router)
+    logits = dev(batch.logits)
+    runs = [[host(x) for x in wf.verify_chain(logits, dev(batch.draft))] for _ in range(2)]
+    assert all(np.array_equal(a, b) for a, b in zip(*runs))
+    al, bo, rows = runs[0]
+    t = oracle.row_argmax(batch.logits, batch.dtype)
+    e_al, e_bo = oracle.verify_chain(t.reshape(batch.B, batch.K + 1), batch.draft)
+    assert np.array_equal(rows, t)
+    assert np.array_equal(al, e_al) and np.array_equal(bo, e_bo)
+    return al
+
+
+def test_single_chain_f32():
+    al = _chain(0)
+    assert 1 <= al[0] <= 17
+
+
+def test_batched_chain_bf16():
+    al = _chain(1)
+    assert 3.0 < al.mean() < 7.0
+
+
+def test_tree_bf16():
+    print("workload tree_bf16", flush=True)
+    batch, _ = make_config(2)
+    logits = dev(batch.logits)
+    args = (logits, dev(batch.parent), dev(batch.draft_ids), dev(batch.d2t))
+    runs = [[host(x) for x in wf.verify_tree(*args)] for _ in range(2)]
+    assert all(np.array_equal(a, b) for a, b in zip(*runs))
+    al, bo, be, rows = runs[0]
+    t = oracle.row_argmax(batch.logits, batch.dtype)
+    e = oracle.verify_tree(t.reshape(batch.B, batch.N), batch.parent, batch.draft_ids, batch.d2t,
+                           batch.V)
+    assert np.array_equal(rows, t)
+    assert np.array_equal(al, e[0]) and np.array_equal(bo, e[1]) and np.array_equal(be, e[2])
+
+
+def test_routed_bf16():
+    print("workload routed_bf16", flush=True)
+    batch, router = make_config(3)
+    ch_gpu, ch_ref = _route(router)
+    assert np.array_equal(ch_ref, batch.layout_choice)
+    # the device choice of the router drives the dispatch, as in the benchmark
+    r = router
+    _, choice = wf.route(dev(r.hidden), dev(r.W1), dev(r.b1), dev(r.W2), float(r.b2), r.tau)
+    logits = dev(batch.logits)
+    args = (logits, dev(batch.offsets), batch.rows, choice, dev(batch.chain_draft),
+            dev(batch.parent), dev(batch.draft_ids), dev(batch.d2t))
+    runs = [[host(x) for x in wf.verify_routed(*args)] for _ in range(2)]
+    assert all(np.array_equal(a, b) for a, b in zip(*runs))
+    al, bo, be, rows = runs[0]
+    t = oracle.row_argmax(batch.logits, batch.dtype)
+    e = oracle.verify_routed(t, batch.offsets, ch_ref, batch.K, batch.chain_draft, batch.N,
+                             batch.parent, batch.draft_ids, batch.d2t, batch.V)
+    assert np.array_equal(rows, t)
+    assert np.array_equal(al, e[0]) and np.array_equal(bo, e[1]) and np.array_equal(be, e[2])
+    assert al.min() >= 1
+
+
+@pytest.mark.parametrize("rnd", [0, 57])
+def test_sweep_bf16(rnd):
+    al = _chain(4, rnd)
+    assert 4.0 < al.mean() < 5.8
