@@ -23,21 +23,28 @@ __device__ inline void take_better(float& bv, int& bi, float v, int i) {
 }
 
 // t_s[i] = argmax of row (row0 + i) for i < nrows; row_argmax[row0 + i] too when given.
+// A group of G lanes (the power of two >= splits, at most 64) merges one row, so
+// a pass over the workgroup covers 256 / G rows with all their loads in flight.
 __device__ void merge_rows(const Partial* __restrict__ part, int splits, int row0, int nrows,
                            int* t_s, int* __restrict__ row_argmax) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = wave; i < nrows; i += kWaves) {
-    const Partial* p = part + static_cast<int64_t>(row0 + i) * splits;
+  int G = 1;
+  while (G < splits && G < 64) G <<= 1;
+  const int per_pass = kThreads / G;
+  const int sl = threadIdx.x & (G - 1);
+  for (int base = 0; base < nrows; base += per_pass) {
+    const int i = base + threadIdx.x / G;
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for (int s = lane; s < splits; s += 64) take_better(bv, bi, p[s].val, p[s].idx);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
+    if (i < nrows) {
+      const Partial* p = part + static_cast<int64_t>(row0 + i) * splits;
+      for (int s = sl; s < splits; s += G) take_better(bv, bi, p[s].val, p[s].idx);
+    }
+    for (int off = G >> 1; off > 0; off >>= 1) {
       const float ov = __shfl_xor(bv, off);
       const int oi = __shfl_xor(bi, off);
       take_better(bv, bi, ov, oi);
     }
-    if (lane == 0) {
+    if (sl == 0 && i < nrows) {
       if (i < kMaxSeqRows) t_s[i] = bi;
       if (row_argmax) row_argmax[row0 + i] = bi;
     }

@@ -6,8 +6,8 @@
 // reads it once with 16-byte loads, 256 threads side by side so every wave64
 // load instruction covers 1 KiB of contiguous memory.  A thread keeps its
 // running maximum and the 16-byte vector where it first reached it (strict
-// ">" in increasing index order keeps the earliest), and only at the end
-// re-reads that one vector to recover the element index.  The per-chunk
+// ">" in increasing index order keeps the earliest) together with that
+// vector's data, and recovers the element index from it at the end.  The per-chunk
 // (max, index) pair is reduced across the wave with cross-lane shuffles and
 // across the four waves in LDS; ties go to the lower index at every level.
 #include <math.h>
@@ -99,8 +99,11 @@ __global__ __launch_bounds__(kThreads) void argmax_sweep_kernel(
   const int v0 = c * chunk_vecs;
   const int v1 = min(v0 + chunk_vecs, nvec);
 
+  // The vector where `best` was first reached stays in registers, so the index
+  // is recovered without a dependent re-load after the stream.
   float best = -INFINITY;
-  int bestv = v0 + tid;  // vector where `best` was first reached
+  int bestv = -1;
+  u32x4 bestd = {0u, 0u, 0u, 0u};
   int v = v0 + tid;
   for (; v + (kUnroll - 1) * kThreads < v1; v += kUnroll * kThreads) {
     u32x4 d[kUnroll];
@@ -112,20 +115,25 @@ __global__ __launch_bounds__(kThreads) void argmax_sweep_kernel(
       if (m > best) {
         best = m;
         bestv = v + u * kThreads;
+        bestd = d[u];
       }
     }
   }
   for (; v < v1; v += kThreads) {
-    const float m = E::vmax(load16(vp + v));
+    const u32x4 d = load16(vp + v);
+    const float m = E::vmax(d);
     if (m > best) {
       best = m;
       bestv = v;
+      bestd = d;
     }
   }
 
   int idx = INT_MAX;
   if (v0 + tid < v1) {
-    idx = bestv * E::kPerVec + E::first_equal(vp[bestv], best);
+    // No element above -inf (all -inf, or NaN): the thread's first element is
+    // the first occurrence of -inf, and a valid index in every case.
+    idx = bestv >= 0 ? bestv * E::kPerVec + E::first_equal(bestd, best) : (v0 + tid) * E::kPerVec;
   } else {
     best = -INFINITY;
   }

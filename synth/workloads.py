@@ -81,6 +81,8 @@ def _planted_logits(seed: int, rnd: int, seq: int, planted: np.ndarray, V: int, 
 
 
 def _other_id(rng: np.random.Generator, V: int, avoid: int) -> int:
+    if V == 1:
+        return avoid  # a one-token vocabulary has no other id
     o = int(rng.integers(0, V - 1))
     return o + 1 if o >= avoid else o
 
