@@ -58,8 +58,10 @@ const char* whiflash_status_string(int32_t status) {
 
 size_t whiflash_route_workspace_bytes(int32_t B, int32_t m) {
   if (B <= 0 || m <= 0) return 0;
-  // The GEMV path needs B * m partials; the MFMA path fewer.
-  return round_up(static_cast<size_t>(B) * static_cast<size_t>(m) * sizeof(float), kWorkspaceAlign);
+  // Pre-activation partials zp[slices][B][m] (float32), slices bounded independently of d.
+  const size_t slices = static_cast<size_t>(wf::router_max_slices(B, m));
+  return round_up(slices * static_cast<size_t>(B) * static_cast<size_t>(m) * sizeof(float),
+                  kWorkspaceAlign);
 }
 
 size_t whiflash_verify_workspace_bytes(int32_t total_rows, int32_t V) {
@@ -76,17 +78,17 @@ int32_t whiflash_route(const void* hidden, int32_t dtype, int32_t B, int32_t d, 
   if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
   if (B == 0) return WF_OK;
   if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
-  if (static_cast<int64_t>(B) * m > INT32_MAX || static_cast<int64_t>(m) * d > (int64_t{1} << 40))
+  if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
     return WF_ERR_SHAPE;
   const int32_t s = check_workspace(workspace, workspace_bytes, whiflash_route_workspace_bytes(B, m));
   if (s != WF_OK) return s;
-  float* part = static_cast<float*>(workspace);
-  const bool mfma = wf::router_use_mfma(dtype, B, d, hidden, W1);
-  const int32_t P = wf::router_partials(B, m, mfma);
-  hipError_t e = mfma ? wf::launch_router_mfma(hidden, B, d, W1, b1, m, W2, part, stream)
-                      : wf::launch_router_gemv(hidden, dtype, B, d, W1, b1, m, W2, part, stream);
-  if (e != hipSuccess) return WF_ERR_LAUNCH;
-  return launch_status(wf::launch_router_reduce(part, P, B, b2, tau, delta_al, choice, stream));
+  float* zp = static_cast<float*>(workspace);
+  const wf::RouterPlan plan = wf::router_plan(dtype, B, d, m, hidden, W1);
+  if (wf::launch_router_stage1(plan, hidden, dtype, B, d, W1, m, zp, stream) != hipSuccess)
+    return WF_ERR_LAUNCH;
+  return launch_status(wf::launch_router_finish(plan, dtype, zp, B, m, b1, W2, b2, tau, delta_al,
+                                                choice, stream));
 }
 
 int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int32_t K, int32_t V,

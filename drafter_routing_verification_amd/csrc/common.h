@@ -49,20 +49,27 @@ hipError_t launch_finalize_routed(const Partial* part, int32_t splits, int32_t B
                                   int32_t* bonus, int32_t* best_node, int32_t* row_argmax,
                                   hipStream_t stream);
 
-// Router: partial second-layer sums part[b * P + p] over P slices of the m
-// hidden units, then a fixed-order reduction to delta_al and the threshold.
-int32_t router_partials(int32_t B, int32_t m, bool mfma);
-bool router_use_mfma(int dtype, int32_t B, int32_t d, const void* hidden, const void* W1);
+// Router: stage 1 writes pre-activation partial sums zp[s][b][j] over `slices`
+// slices of the hidden size; stage 2 finishes each sequence.
+constexpr int32_t kMaxRouterSlices = 8;
 
-hipError_t launch_router_gemv(const void* hidden, int dtype, int32_t B, int32_t d, const void* W1,
-                              const float* b1, int32_t m, const void* W2, float* part,
-                              hipStream_t stream);
+struct RouterPlan {
+  bool mfma;       // bf16 MFMA tiles (else the wave-per-unit GEMV, one slice)
+  int32_t slices;  // slices of the hidden size (workgroups along k)
+  int32_t kslice;  // hidden-size columns per slice
+};
 
-hipError_t launch_router_mfma(const void* hidden, int32_t B, int32_t d, const void* W1,
-                              const float* b1, int32_t m, const void* W2, float* part,
-                              hipStream_t stream);
+// Upper bound of slices for (B, m), independent of d: sizes the workspace.
+int32_t router_max_slices(int32_t B, int32_t m);
+RouterPlan router_plan(int dtype, int32_t B, int32_t d, int32_t m, const void* hidden,
+                       const void* W1);
 
-hipError_t launch_router_reduce(const float* part, int32_t P, int32_t B, const float* b2, float tau,
-                                float* delta_al, int32_t* choice, hipStream_t stream);
+hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, int dtype, int32_t B,
+                                int32_t d, const void* W1, int32_t m, float* zp,
+                                hipStream_t stream);
+
+hipError_t launch_router_finish(const RouterPlan& plan, int dtype, const float* zp, int32_t B,
+                                int32_t m, const float* b1, const void* W2, const float* b2,
+                                float tau, float* delta_al, int32_t* choice, hipStream_t stream);
 
 }  // namespace wf

@@ -1,18 +1,19 @@
 // WhiFlash-Neural router (WhiFlash paper, section 3.3.2 and Appendix A):
 //   dal[b] = W2 . GELU(W1 h_b + b1) + b2,  choice[b] = dal[b] > tau.
-// Two first-stage kernels write fixed partial sums of the second layer,
-// part[b * P + p] = sum over hidden units j of slice p of W2[j] * GELU(z[b, j]):
-//   - router_gemv: small batches or float32.  One wave64 per hidden unit j
-//     streams row j of W1 once with coalesced 16-byte loads and dots it with up
-//     to 8 hidden states at a time; the dot is reduced across the wave with
-//     shuffles, then GELU and the W2 product run in float32.  P = m.
-//   - router_mfma: bf16 batches of 16 or more.  A workgroup computes a 32 (j) x
-//     32 (b) tile of z with v_mfma_f32_16x16x32_bf16 (float32 accumulate), its
-//     eight waves splitting the hidden size; GELU and W2 are applied to the
-//     summed accumulators and each 16-unit slice of j yields one partial.
-//     P = 2 * ceil(m / 32).
-// router_reduce then sums the P partials of each sequence in a fixed order, so
-// results are bitwise reproducible run to run, adds b2 and thresholds.
+// Stage 1 writes pre-activation partial sums zp[s][b][j] of z = W1 h_b over KS
+// slices s of the hidden size:
+//   - router_gemv_kernel (small batches or float32, KS = 1): one wave64 per
+//     hidden unit j streams row j of W1 once with coalesced 16-byte loads and
+//     dots it with up to 8 hidden states, reduced across the wave by shuffles.
+//   - router_mfma_kernel (bf16 batches of 16 or more): a workgroup owns a
+//     32 (j) x 64 (b) tile and one slice of the hidden size.  All of its loads
+//     are issued up front as row-contiguous 16-byte loads, staged chunk by
+//     chunk through LDS, and multiplied with v_mfma_f32_16x16x32_bf16 (float32
+//     accumulate).  Splitting the hidden size across workgroups keeps every CU
+//     busy while each moves ~120 KB instead of ~300 KB.
+// Stage 2, router_finish_kernel, one workgroup per sequence: sums the KS
+// partials, adds b1, applies GELU and W2, sums over j and adds b2, all in
+// float32 and in a fixed order (bitwise reproducible), then thresholds.
 #include <math.h>
 
 #include "common.h"
@@ -20,10 +21,14 @@
 namespace wf {
 namespace {
 
-constexpr int kTileJ = 32;          // hidden units per MFMA workgroup tile
-constexpr int kTileB = 32;          // sequences per MFMA workgroup tile
-constexpr int kMfmaWaves = 8;       // waves splitting the hidden size of one tile
 constexpr int kGemvUnroll = 4;      // 16-byte vectors in flight per lane in the GEMV
+constexpr int kMfmaTileJ = 32;      // hidden units per MFMA workgroup tile
+constexpr int kMfmaTileB = 64;      // sequences per MFMA workgroup tile
+constexpr int kChunk = 128;         // hidden-size columns staged through LDS at a time
+constexpr int kStageRows = kMfmaTileJ + kMfmaTileB;
+constexpr int kStageStride = kChunk + 8;                      // padded row (elements)
+constexpr int kPiecesPerThread = kStageRows * (kChunk / 8) / kThreads;  // 16-byte pieces
+constexpr int kChunksInFlight = 5;  // chunks whose loads are issued together
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -55,13 +60,14 @@ __device__ inline float dot16(u32x4 a, u32x4 b, float acc) {
   return acc;
 }
 
-// One wave per hidden unit j and NB sequences: row j of W1 is streamed once.
+// One wave per hidden unit j and NB sequences: row j of W1 is streamed once;
+// writes zp[b][j] = W1[j] . h_b.
 // VEC: rows are 16-byte aligned and d is a multiple of the vector width, so
 // each lane reads 16-byte vectors, kGemvUnroll of them in flight.
 template <int DT, int NB, bool VEC>
 __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
-    const void* __restrict__ hidden, int B, int d, const void* __restrict__ W1,
-    const float* __restrict__ b1, int m, const void* __restrict__ W2, float* __restrict__ part) {
+    const void* __restrict__ hidden, int B, int d, const void* __restrict__ W1, int m,
+    float* __restrict__ zp) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int b0 = blockIdx.y * NB;
@@ -106,110 +112,142 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
         if (q < nb) acc[q] = fmaf(w, load_elem<DT>(hidden, static_cast<int64_t>(b0 + q) * d + k), acc[q]);
     }
   }
-  const float bias = b1 ? b1[j] : 0.f;
-  const float w2 = load_elem<DT>(W2, j);
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
     float s = acc[q];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == q && q < nb) part[static_cast<int64_t>(b0 + q) * m + j] = w2 * gelu(s + bias);
+    if (lane == q && q < nb) zp[static_cast<int64_t>(b0 + q) * m + j] = s;
   }
 }
 
-// 16 bytes (8 bf16) of row `r` at column k, or zeros outside the matrix.
-__device__ inline bf16x8 frag(const unsigned short* base, int r, int rows, int d, int k) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (r < rows && k < d) v = *reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(r) * d + k);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// One workgroup per 32 (hidden units j) x 32 (sequences b) tile of z^T; its
-// eight waves split the hidden size into interleaved 32-wide k steps, and
-// their accumulators are summed in LDS in a fixed order.
+// One workgroup = 4 waves per 32 (j) x 64 (b) tile of z^T and one slice
+// [k0, k1) of the hidden size.  Rows 0..31 of the staging area hold W1 rows
+// j0.., rows 32..95 hold hidden rows bb0..; each row chunk is kChunk wide.
+// Wave w computes the 16 x 16 accumulators (j-subtile w & 1) x (b-subtiles
+// 2 (w >> 1) and 2 (w >> 1) + 1).
 // Operand layout of v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16) of
 // the A tile and column (l % 16) of the B tile, 8 consecutive k values starting
 // at 8 * (l / 16); the accumulator of lane l holds rows 4 * (l / 16) + i,
 // i = 0..3, of column l % 16.
-__global__ __launch_bounds__(kMfmaWaves * 64) void router_mfma_kernel(
+__global__ __launch_bounds__(kThreads) void router_mfma_kernel(
     const unsigned short* __restrict__ hidden, int B, int d, const unsigned short* __restrict__ W1,
-    const float* __restrict__ b1, int m, const unsigned short* __restrict__ W2, int P,
-    float* __restrict__ part) {
-  __shared__ float red[kMfmaWaves][16][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int j0 = blockIdx.x * kTileJ;
-  const int bb0 = blockIdx.y * kTileB;
-  const int r = lane & 15, kq = (lane >> 4) * 8;
-  f32x4 acc[2][2];
+    int m, int kslice, float* __restrict__ zp) {
+  __shared__ __attribute__((aligned(16))) unsigned short stage[kStageRows * kStageStride];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j0 = blockIdx.x * kMfmaTileJ, bb0 = blockIdx.y * kMfmaTileB, slice = blockIdx.z;
+  const int k0 = slice * kslice, k1 = min(d, k0 + kslice);
+  const int r = lane & 15, g = lane >> 4;
+  const int a = w & 1, bq = (w >> 1) * 2;
+  // Rows this thread stages: row = i * 16 + (tid >> 4), piece column tid & 15.
+  const int prow = tid >> 4, pcol = (tid & 15) * 8;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int nchunks = (k1 - k0 + kChunk - 1) / kChunk;
+  for (int c0 = 0; c0 < nchunks; c0 += kChunksInFlight) {
+    u32x4 buf[kChunksInFlight][kPiecesPerThread];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int c = 0; c < kChunksInFlight; ++c) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int steps = (d + 31) / 32;
-  // All operands of up to kU of this wave's k steps are loaded before their
-  // MFMAs, so a hidden size of up to kU * 8 * 32 costs one memory round trip.
-  constexpr int kU = 10;
-  for (int base = w; base < steps; base += kU * kMfmaWaves) {
-    bf16x8 a0[kU], a1[kU], h0[kU], h1[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int k = (base + u * kMfmaWaves) * 32 + kq;  // frag() zero-fills k >= d
-      a0[u] = frag(W1, j0 + r, m, d, k);
-      a1[u] = frag(W1, j0 + 16 + r, m, d, k);
-      h0[u] = frag(hidden, bb0 + r, B, d, k);
-      h1[u] = frag(hidden, bb0 + 16 + r, B, d, k);
+      for (int i = 0; i < kPiecesPerThread; ++i) {
+        const int row = i * 16 + prow;
+        const int k = k0 + (c0 + c) * kChunk + pcol;
+        const unsigned short* src = nullptr;
+        if (row < kMfmaTileJ) {
+          if (j0 + row < m) src = W1 + static_cast<int64_t>(j0 + row) * d;
+        } else if (bb0 + row - kMfmaTileJ < B) {
+          src = hidden + static_cast<int64_t>(bb0 + row - kMfmaTileJ) * d;
+        }
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (src != nullptr && c0 + c < nchunks && k < k1) v = *reinterpret_cast<const u32x4*>(src + k);
+        buf[c][i] = v;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (base + u * kMfmaWaves < steps) {
-        acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[u], h0[u], acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[u], h1[u], acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[u], h0[u], acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[u], h1[u], acc[1][1], 0, 0, 0);
+    for (int c = 0; c < kChunksInFlight; ++c) {
+      if (c0 + c >= nchunks) break;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kPiecesPerThread; ++i)
+        *reinterpret_cast<u32x4*>(&stage[(i * 16 + prow) * kStageStride + pcol]) = buf[c][i];
+      __syncthreads();
+#pragma unroll
+      for (int st = 0; st < kChunk / 32; ++st) {
+        const int col = st * 32 + g * 8;
+        const bf16x8 fa = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&stage[(a * 16 + r) * kStageStride + col]));
+        const bf16x8 f0 = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(
+                        &stage[(kMfmaTileJ + bq * 16 + r) * kStageStride + col]));
+        const bf16x8 f1 = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(
+                        &stage[(kMfmaTileJ + (bq + 1) * 16 + r) * kStageStride + col]));
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f1, acc1, 0, 0, 0);
+      }
+    }
+  }
+  // z partials: lane holds j = j0 + 16a + 4g + i for one b per accumulator.
+  const int jb = j0 + a * 16 + g * 4;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int b = bb0 + (bq + q) * 16 + r;
+    if (b >= B) continue;
+    const f32x4 v = q == 0 ? acc0 : acc1;
+    float* dst = zp + (static_cast<int64_t>(slice) * B + b) * m + jb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (jb + i < m) dst[i] = v[i];
+  }
+}
+
+// One workgroup per sequence: fixed-order sums over slices, units, waves.
+// Each thread owns up to kFinishPer hidden units per pass; all their partials,
+// biases and W2 entries are loaded before any is used, so a pass costs one
+// memory round trip.
+constexpr int kFinishPer = 4;
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void router_finish_kernel(
+    const float* __restrict__ zp, int KS, int B, int m, const float* __restrict__ b1,
+    const void* __restrict__ W2, const float* __restrict__ b2, float tau,
+    float* __restrict__ delta_al, int32_t* __restrict__ choice) {
+  __shared__ float red[kWaves];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int64_t slice_stride = static_cast<int64_t>(B) * m;
+  const float* zb = zp + static_cast<int64_t>(b) * m;
+  float acc = 0.f;
+  for (int base = 0; base < m; base += kThreads * kFinishPer) {
+    float part[kMaxRouterSlices][kFinishPer];
+    float bias[kFinishPer], w2[kFinishPer];
+#pragma unroll
+    for (int u = 0; u < kFinishPer; ++u) {
+      const int j = base + u * kThreads + tid;
+      const bool ok = j < m;
+#pragma unroll
+      for (int s = 0; s < kMaxRouterSlices; ++s)
+        part[s][u] = (ok && s < KS) ? zb[s * slice_stride + j] : 0.f;
+      bias[u] = (ok && b1) ? b1[j] : 0.f;
+      w2[u] = ok ? load_elem<DT>(W2, j) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kFinishPer; ++u) {
+      if (base + u * kThreads + tid < m) {
+        float z = 0.f;
+#pragma unroll
+        for (int s = 0; s < kMaxRouterSlices; ++s)
+          if (s < KS) z += part[s][u];
+        acc += w2[u] * gelu(z + bias[u]);
       }
     }
   }
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[w][a * 8 + c * 4 + i][lane] = acc[a][c][i];
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
   __syncthreads();
-  // Waves 0..3 each finish one 16 (j) x 16 (b) accumulator: fixed-order sum over
-  // the eight waves, GELU and W2, then the sum over its 16 hidden units.
-  if (w < 4) {
-    const int a = w >> 1, c = w & 1;
-    float sacc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float z = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kMfmaWaves; ++ww) z += red[ww][a * 8 + c * 4 + i][lane];
-      const int j = j0 + a * 16 + (lane >> 4) * 4 + i;
-      if (j < m) sacc += bf16_to_f32(W2[j]) * gelu(z + (b1 ? b1[j] : 0.f));
-    }
-    sacc += __shfl_xor(sacc, 16);
-    sacc += __shfl_xor(sacc, 32);
-    const int b = bb0 + c * 16 + r;
-    if (lane < 16 && b < B) part[static_cast<int64_t>(b) * P + blockIdx.x * 2 + a] = sacc;
-  }
-}
-
-// One wave per sequence: fixed-order sum of its P partials, + b2, threshold.
-__global__ __launch_bounds__(kThreads) void router_reduce_kernel(
-    const float* __restrict__ part, int P, int B, const float* __restrict__ b2, float tau,
-    float* __restrict__ delta_al, int32_t* __restrict__ choice) {
-  const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (b >= B) return;
-  const float* p = part + static_cast<int64_t>(b) * P;
-  float s = 0.f;
-  for (int i = lane; i < P; i += 64) s += p[i];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) {
-    const float v = s + (b2 ? *b2 : 0.f);
+  if (tid == 0) {
+    float v = red[0];
+    for (int w = 1; w < kWaves; ++w) v += red[w];
+    v += b2 ? *b2 : 0.f;
     delta_al[b] = v;
     choice[b] = v > tau ? 1 : 0;
   }
@@ -217,67 +255,82 @@ __global__ __launch_bounds__(kThreads) void router_reduce_kernel(
 
 }  // namespace
 
-bool router_use_mfma(int dtype, int32_t B, int32_t d, const void* hidden, const void* W1) {
+RouterPlan router_plan(int dtype, int32_t B, int32_t d, int32_t m, const void* hidden,
+                       const void* W1) {
+  RouterPlan p{false, 1, d};
   const bool aligned = (reinterpret_cast<uintptr_t>(hidden) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(W1) % 16 == 0) && (d % 8 == 0);
-  return dtype == WF_BF16 && B >= 16 && aligned;
+  if (dtype != WF_BF16 || B < 16 || !aligned) return p;
+  p.mfma = true;
+  int ks = router_max_slices(B, m);
+  const int max_by_d = (d + kChunk - 1) / kChunk;
+  if (ks > max_by_d) ks = max_by_d;
+  const int per = (d + ks - 1) / ks;
+  p.kslice = (per + kChunk - 1) / kChunk * kChunk;
+  p.slices = (d + p.kslice - 1) / p.kslice;
+  return p;
 }
 
-int32_t router_partials(int32_t B, int32_t m, bool mfma) {
-  (void)B;
-  return mfma ? 2 * ((m + kTileJ - 1) / kTileJ) : m;
+int32_t router_max_slices(int32_t B, int32_t m) {
+  // Split the hidden size until the grid covers ~256 workgroups (one per CU).
+  const int64_t tiles = static_cast<int64_t>((m + kMfmaTileJ - 1) / kMfmaTileJ) *
+                        ((B + kMfmaTileB - 1) / kMfmaTileB);
+  int64_t ks = tiles > 0 ? 256 / tiles : 1;
+  if (ks < 1) ks = 1;
+  if (ks > kMaxRouterSlices) ks = kMaxRouterSlices;
+  return static_cast<int32_t>(ks);
 }
 
 template <int DT, int NB, bool VEC>
 static void gemv_launch(dim3 grid, hipStream_t stream, const void* hidden, int32_t B, int32_t d,
-                        const void* W1, const float* b1, int32_t m, const void* W2, float* part) {
+                        const void* W1, int32_t m, float* zp) {
   hipLaunchKernelGGL((router_gemv_kernel<DT, NB, VEC>), grid, dim3(kThreads), 0, stream, hidden, B,
-                     d, W1, b1, m, W2, part);
+                     d, W1, m, zp);
 }
 
 template <int DT, bool VEC>
-static void gemv_dispatch(const void* hidden, int32_t B, int32_t d, const void* W1, const float* b1,
-                          int32_t m, const void* W2, float* part, hipStream_t stream) {
+static void gemv_dispatch(const void* hidden, int32_t B, int32_t d, const void* W1, int32_t m,
+                          float* zp, hipStream_t stream) {
   const unsigned gx = (m + kWaves - 1) / kWaves;
-  if (B == 1) gemv_launch<DT, 1, VEC>(dim3(gx, 1), stream, hidden, B, d, W1, b1, m, W2, part);
-  else if (B <= 2) gemv_launch<DT, 2, VEC>(dim3(gx, 1), stream, hidden, B, d, W1, b1, m, W2, part);
-  else if (B <= 4) gemv_launch<DT, 4, VEC>(dim3(gx, 1), stream, hidden, B, d, W1, b1, m, W2, part);
-  else gemv_launch<DT, 8, VEC>(dim3(gx, (B + 7) / 8), stream, hidden, B, d, W1, b1, m, W2, part);
+  if (B == 1) gemv_launch<DT, 1, VEC>(dim3(gx, 1), stream, hidden, B, d, W1, m, zp);
+  else if (B <= 2) gemv_launch<DT, 2, VEC>(dim3(gx, 1), stream, hidden, B, d, W1, m, zp);
+  else if (B <= 4) gemv_launch<DT, 4, VEC>(dim3(gx, 1), stream, hidden, B, d, W1, m, zp);
+  else gemv_launch<DT, 8, VEC>(dim3(gx, (B + 7) / 8), stream, hidden, B, d, W1, m, zp);
 }
 
-hipError_t launch_router_gemv(const void* hidden, int dtype, int32_t B, int32_t d, const void* W1,
-                              const float* b1, int32_t m, const void* W2, float* part,
-                              hipStream_t stream) {
+hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, int dtype, int32_t B,
+                                int32_t d, const void* W1, int32_t m, float* zp,
+                                hipStream_t stream) {
+  if (plan.mfma) {
+    const dim3 grid((m + kMfmaTileJ - 1) / kMfmaTileJ, (B + kMfmaTileB - 1) / kMfmaTileB,
+                    plan.slices);
+    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(kThreads), 0, stream,
+                       static_cast<const unsigned short*>(hidden), B, d,
+                       static_cast<const unsigned short*>(W1), m, plan.kslice, zp);
+    return hipGetLastError();
+  }
   const int per = dtype == WF_BF16 ? 8 : 4;
   const bool vec = (reinterpret_cast<uintptr_t>(hidden) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(W1) % 16 == 0) && (d % per == 0);
   if (dtype == WF_BF16) {
-    if (vec) gemv_dispatch<WF_BF16, true>(hidden, B, d, W1, b1, m, W2, part, stream);
-    else gemv_dispatch<WF_BF16, false>(hidden, B, d, W1, b1, m, W2, part, stream);
+    if (vec) gemv_dispatch<WF_BF16, true>(hidden, B, d, W1, m, zp, stream);
+    else gemv_dispatch<WF_BF16, false>(hidden, B, d, W1, m, zp, stream);
   } else {
-    if (vec) gemv_dispatch<WF_F32, true>(hidden, B, d, W1, b1, m, W2, part, stream);
-    else gemv_dispatch<WF_F32, false>(hidden, B, d, W1, b1, m, W2, part, stream);
+    if (vec) gemv_dispatch<WF_F32, true>(hidden, B, d, W1, m, zp, stream);
+    else gemv_dispatch<WF_F32, false>(hidden, B, d, W1, m, zp, stream);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_router_mfma(const void* hidden, int32_t B, int32_t d, const void* W1,
-                              const float* b1, int32_t m, const void* W2, float* part,
-                              hipStream_t stream) {
-  const int tiles = (m + kTileJ - 1) / kTileJ;
-  const int P = 2 * tiles;
-  const dim3 grid(tiles, (B + kTileB - 1) / kTileB);
-  hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(kMfmaWaves * 64), 0, stream,
-                     static_cast<const unsigned short*>(hidden), B, d,
-                     static_cast<const unsigned short*>(W1), b1, m,
-                     static_cast<const unsigned short*>(W2), P, part);
-  return hipGetLastError();
-}
-
-hipError_t launch_router_reduce(const float* part, int32_t P, int32_t B, const float* b2, float tau,
-                                float* delta_al, int32_t* choice, hipStream_t stream) {
-  hipLaunchKernelGGL(router_reduce_kernel, dim3((B + kWaves - 1) / kWaves), dim3(kThreads), 0,
-                     stream, part, P, B, b2, tau, delta_al, choice);
+hipError_t launch_router_finish(const RouterPlan& plan, int dtype, const float* zp, int32_t B,
+                                int32_t m, const float* b1, const void* W2, const float* b2,
+                                float tau, float* delta_al, int32_t* choice, hipStream_t stream) {
+  if (dtype == WF_BF16)
+    hipLaunchKernelGGL(router_finish_kernel<WF_BF16>, dim3(B), dim3(kThreads), 0, stream, zp,
+                       plan.slices, B, m, b1, W2, b2, tau, delta_al, choice);
+  else
+    hipLaunchKernelGGL(router_finish_kernel<WF_F32>, dim3(B), dim3(kThreads), 0, stream, zp,
+                       plan.slices, B, m, b1, W2, b2, tau, delta_al, choice);
   return hipGetLastError();
 }
 
