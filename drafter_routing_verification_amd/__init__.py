@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     verify_tree(logits, parent, draft_ids, d2t)           -> (accept_len, bonus, best_node, row_argmax)
     verify_routed(logits, row_offsets, total_rows, choice, chain_draft, parent, draft_ids, d2t)
                                                           -> (accept_len, bonus, best_node, row_argmax)
+    route_entropy(logits, pos, tau, row0=None, rows_per_seq=0)  -> (entropy, choice)
 """
 
 from ._binding import (  # noqa: F401
@@ -27,6 +28,9 @@ from ._binding import (  # noqa: F401
     verify_chain,
     verify_tree,
     verify_routed,
+    route_entropy,
+    entropy_workspace_bytes,
+    whiflash_route_entropy,
     whiflash_route,
     whiflash_verify_chain,
     whiflash_verify_tree,

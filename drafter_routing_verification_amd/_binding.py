@@ -31,6 +31,9 @@ _SIGNATURES = {
                                        _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_verify_tree": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
                                       _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "whiflash_entropy_workspace_bytes": (_c_sz, [_c_i32, _c_i32]),
+    "whiflash_route_entropy": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_p, _c_i32,
+                                        _c_p, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_verify_routed": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_i32, _c_p,
                                         _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p,
                                         _c_p, _c_p, _c_p, _c_sz, _c_p]),
@@ -89,6 +92,14 @@ def whiflash_verify_tree(*args):
 
 def whiflash_verify_routed(*args):
     return lib().whiflash_verify_routed(*args)
+
+
+def whiflash_route_entropy(*args):
+    return lib().whiflash_route_entropy(*args)
+
+
+def entropy_workspace_bytes(B: int, V: int) -> int:
+    return int(lib().whiflash_entropy_workspace_bytes(B, V))
 
 
 # ----------------------------------------------------------------------------- helpers
@@ -277,3 +288,32 @@ def verify_routed(logits, row_offsets, total_rows: int, choice, chain_draft, par
                                   0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(logits, stream)))
     return accept_len, bonus, best_node, row_argmax
+
+
+def route_entropy(logits, pos, tau: float, *, row0=None, rows_per_seq: int = 0, entropy=None,
+                  choice=None, workspace=None, stream=None):
+    """WhiFlash-Entropy policy.  logits [total_rows, V] (or [B, R, V]); pos [B] int32 position of
+    each sequence's final accepted row within the sequence; row0 [B] int32 first row of each
+    sequence, or None with rows_per_seq (row0[b] = b * rows_per_seq)."""
+    _device_tensor(pos, "pos")
+    B = pos.numel()
+    if logits.dim() == 3:
+        total_rows = logits.shape[0] * logits.shape[1]
+    else:
+        total_rows = logits.shape[0]
+    V, stride = _rows_view(logits, total_rows)
+    _i32(pos, "pos", B)
+    if row0 is not None:
+        _i32(row0, "row0")
+        if row0.numel() < B:
+            raise ValueError("row0 must hold at least B entries")
+    dev = logits.device
+    entropy = torch.empty(B, dtype=torch.float32, device=dev) if entropy is None else entropy
+    choice = torch.empty(B, dtype=torch.int32, device=dev) if choice is None else choice
+    ws = _workspace(workspace, entropy_workspace_bytes(B, V), dev)
+    _check(whiflash_route_entropy(_ptr(logits), _dtype_code(logits), total_rows, V, stride, B,
+                                  _ptr(row0), rows_per_seq, _ptr(pos), float(tau), _ptr(entropy),
+                                  _ptr(choice), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(logits, stream)))
+    return entropy, choice

@@ -165,4 +165,28 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
                                                   stream));
 }
 
+size_t whiflash_entropy_workspace_bytes(int32_t B, int32_t V) {
+  if (B <= 0 || V <= 0) return 0;
+  const wf::SweepPlan plan = wf::entropy_plan(B, V);
+  return round_up(static_cast<size_t>(B) * plan.splits * 16, kWorkspaceAlign);
+}
+
+int32_t whiflash_route_entropy(const void* logits, int32_t dtype, int32_t total_rows, int32_t V,
+                               int64_t row_stride, int32_t B, const int32_t* row0,
+                               int32_t rows_per_seq, const int32_t* pos, float tau,
+                               float* entropy, int32_t* choice, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || total_rows < 0 || (row0 == nullptr && rows_per_seq < 0)) return WF_ERR_SHAPE;
+  int32_t s = check_logits(logits, dtype, total_rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (B > INT32_MAX / 64) return WF_ERR_SHAPE;
+  if (!pos || !entropy || !choice) return WF_ERR_NULL;
+  if ((s = check_workspace(workspace, workspace_bytes, whiflash_entropy_workspace_bytes(B, V))) != WF_OK)
+    return s;
+  return launch_status(wf::launch_entropy(logits, dtype, row_stride, total_rows, V, B, row0,
+                                          rows_per_seq, pos, tau, entropy, choice, workspace,
+                                          stream));
+}
+
 }  // extern "C"

@@ -72,4 +72,12 @@ hipError_t launch_router_finish(const RouterPlan& plan, int dtype, const float* 
                                 int32_t m, const float* b1, const void* W2, const float* b2,
                                 float tau, float* delta_al, int32_t* choice, hipStream_t stream);
 
+// Entropy policy: partials float4 {m, S, U, -} per (sequence, chunk), then one
+// finish kernel.  Workspace: B * splits * 16 bytes.
+SweepPlan entropy_plan(int32_t B, int32_t V);
+hipError_t launch_entropy(const void* logits, int dtype, int64_t row_stride, int32_t total_rows,
+                          int32_t V, int32_t B, const int32_t* row0, int32_t rows_per_seq,
+                          const int32_t* pos, float tau, float* entropy, int32_t* choice,
+                          void* workspace, hipStream_t stream);
+
 }  // namespace wf

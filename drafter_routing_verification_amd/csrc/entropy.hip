@@ -1,0 +1,190 @@
+// WhiFlash-Entropy policy (WhiFlash paper, section 3.3.1): the entropy of the
+// target's next-token distribution (softmax of one logits row) at each
+// sequence's final accepted position, thresholded into a drafter choice.
+//
+// One streaming pass per selected row.  A workgroup owns one chunk of the row;
+// each thread keeps, in base 2, m = running maximum, S = sum of 2^y and
+// U = sum of y 2^y with y = (x - m) log2(e), rescaling both when m grows:
+// moving to m' multiplies every 2^y by f = 2^d, d = (m - m') log2(e), and
+// shifts every y by d, so S' = S f and U' = (U + d S) f.  Chunks merge the
+// same way, and H = ln 2 (log2 S - U / S).  All merges run in a fixed order.
+#include <math.h>
+
+#include "common.h"
+#include "elem.h"
+
+namespace wf {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kEntUnroll = 4;
+
+struct Ent {
+  float m, S, U;
+};
+
+// Folds (m2, S2, U2) into (m, S, U).
+__device__ inline void ent_merge(Ent& a, const Ent& b) {
+  if (b.S == 0.f) return;
+  if (a.S == 0.f) {
+    a = b;
+    return;
+  }
+  const float M = fmaxf(a.m, b.m);
+  const float da = (a.m - M) * kLog2e, db = (b.m - M) * kLog2e;
+  const float fa = __builtin_amdgcn_exp2f(da), fb = __builtin_amdgcn_exp2f(db);
+  a.U = (a.U + da * a.S) * fa + (b.U + db * b.S) * fb;
+  a.S = a.S * fa + b.S * fb;
+  a.m = M;
+}
+
+__device__ inline Ent shfl_xor(const Ent& e, int off) {
+  return Ent{__shfl_xor(e.m, off), __shfl_xor(e.S, off), __shfl_xor(e.U, off)};
+}
+
+__device__ inline int64_t selected_row(int b, const int32_t* row0, int rows_per_seq,
+                                       const int32_t* pos, int total_rows) {
+  const int p = pos[b];
+  const int64_t r = (row0 ? static_cast<int64_t>(row0[b]) : static_cast<int64_t>(b) * rows_per_seq) + p;
+  return (p >= 0 && r >= 0 && r < total_rows) ? r : -1;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void entropy_partial_kernel(
+    const unsigned char* __restrict__ logits, int64_t row_bytes, int total_rows, int V,
+    const int32_t* __restrict__ row0, int rows_per_seq, const int32_t* __restrict__ pos,
+    int splits, int chunk_vecs, int nvec, float4* __restrict__ part) {
+  using E = Elem<DT>;
+  const int blk = blockIdx.x;
+  const int b = blk / splits;
+  const int c = blk - b * splits;
+  const int64_t row = selected_row(b, row0, rows_per_seq, pos, total_rows);
+  const int tid = threadIdx.x;
+  Ent acc{-INFINITY, 0.f, 0.f};
+  if (row >= 0) {
+    const unsigned char* rowp = logits + row * row_bytes;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rowp);
+    const int v0 = c * chunk_vecs;
+    const int v1 = min(v0 + chunk_vecs, nvec);
+    auto absorb = [&](u32x4 d) {
+      const float mv = E::vmax(d);
+      if (mv > acc.m) {
+        if (acc.S != 0.f) {
+          const float dl = (acc.m - mv) * kLog2e;
+          const float f = __builtin_amdgcn_exp2f(dl);
+          acc.U = (acc.U + dl * acc.S) * f;
+          acc.S *= f;
+        }
+        acc.m = mv;
+      }
+      const float mb = acc.m * kLog2e;
+#pragma unroll
+      for (int k = 0; k < E::kPerVec; ++k) {
+        const float y = fmaf(E::at(d, k), kLog2e, -mb);
+        const float e = __builtin_amdgcn_exp2f(y);
+        acc.S += e;
+        acc.U = fmaf(y, e, acc.U);
+      }
+    };
+    int v = v0 + tid;
+    for (; v + (kEntUnroll - 1) * kThreads < v1; v += kEntUnroll * kThreads) {
+      u32x4 d[kEntUnroll];
+#pragma unroll
+      for (int u = 0; u < kEntUnroll; ++u) d[u] = load16(vp + v + u * kThreads);
+#pragma unroll
+      for (int u = 0; u < kEntUnroll; ++u) absorb(d[u]);
+    }
+    for (; v < v1; v += kThreads) absorb(load16(vp + v));
+    if (c == splits - 1 && tid == 0) {
+      for (int e = nvec * E::kPerVec; e < V; ++e) {
+        const float x = E::scalar(rowp, e);
+        Ent one{x, 1.f, 0.f};
+        ent_merge(acc, one);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const Ent o = shfl_xor(acc, off);
+    ent_merge(acc, o);
+  }
+  __shared__ Ent red[kWaves];
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    Ent t = red[0];
+    for (int w = 1; w < kWaves; ++w) ent_merge(t, red[w]);
+    part[blk] = make_float4(t.m, t.S, t.U, 0.f);
+  }
+}
+
+// One wave per sequence: fixed-order merge of its chunks, H, threshold.
+__global__ __launch_bounds__(kThreads) void entropy_finish_kernel(
+    const float4* __restrict__ part, int splits, int B, const int32_t* __restrict__ row0,
+    int rows_per_seq, const int32_t* __restrict__ pos, int total_rows, float tau,
+    float* __restrict__ entropy, int32_t* __restrict__ choice) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (b >= B) return;
+  Ent acc{-INFINITY, 0.f, 0.f};
+  for (int s = lane; s < splits; s += 64) {
+    const float4 p = part[static_cast<int64_t>(b) * splits + s];
+    ent_merge(acc, Ent{p.x, p.y, p.z});
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const Ent o = shfl_xor(acc, off);
+    ent_merge(acc, o);
+  }
+  if (lane == 0) {
+    const bool valid = selected_row(b, row0, rows_per_seq, pos, total_rows) >= 0 && acc.S > 0.f;
+    const float H = valid ? kLn2 * (__builtin_amdgcn_logf(acc.S) - acc.U / acc.S) : NAN;
+    entropy[b] = H;
+    choice[b] = (valid && H > tau) ? 1 : 0;
+  }
+}
+
+}  // namespace
+
+SweepPlan entropy_plan(int32_t B, int32_t V) {
+  // ~2048 workgroups over the B selected rows, chunks of at least 2048 elements.
+  constexpr int64_t kTargetBlocks = 2048;
+  constexpr int64_t kMinChunk = 2048;
+  const int64_t max_splits = V / kMinChunk > 1 ? V / kMinChunk : 1;
+  int64_t splits = (kTargetBlocks + B - 1) / (B > 0 ? B : 1);
+  if (splits < 1) splits = 1;
+  if (splits > max_splits) splits = max_splits;
+  int64_t chunk = (V + splits - 1) / splits;
+  chunk = (chunk + 7) / 8 * 8;
+  splits = (V + chunk - 1) / chunk;
+  return SweepPlan{static_cast<int32_t>(splits), static_cast<int32_t>(chunk)};
+}
+
+hipError_t launch_entropy(const void* logits, int dtype, int64_t row_stride, int32_t total_rows,
+                          int32_t V, int32_t B, const int32_t* row0, int32_t rows_per_seq,
+                          const int32_t* pos, float tau, float* entropy, int32_t* choice,
+                          void* workspace, hipStream_t stream) {
+  const SweepPlan plan = entropy_plan(B, V);
+  float4* part = static_cast<float4*>(workspace);
+  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(B) * plan.splits);
+  const unsigned char* base = static_cast<const unsigned char*>(logits);
+  if (dtype == WF_BF16) {
+    using E = Elem<WF_BF16>;
+    hipLaunchKernelGGL(entropy_partial_kernel<WF_BF16>, dim3(blocks), dim3(kThreads), 0, stream,
+                       base, row_stride * E::kBytes, total_rows, V, row0, rows_per_seq, pos,
+                       plan.splits, plan.chunk / E::kPerVec, V / E::kPerVec, part);
+  } else {
+    using E = Elem<WF_F32>;
+    hipLaunchKernelGGL(entropy_partial_kernel<WF_F32>, dim3(blocks), dim3(kThreads), 0, stream,
+                       base, row_stride * E::kBytes, total_rows, V, row0, rows_per_seq, pos,
+                       plan.splits, plan.chunk / E::kPerVec, V / E::kPerVec, part);
+  }
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(entropy_finish_kernel, dim3((B + kWaves - 1) / kWaves), dim3(kThreads), 0,
+                     stream, part, plan.splits, B, row0, rows_per_seq, pos, total_rows, tau, entropy,
+                     choice);
+  return hipGetLastError();
+}
+
+}  // namespace wf

@@ -169,6 +169,34 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
                                int32_t* row_argmax,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes whiflash_route_entropy needs for B sequences and rows of V
+ * entries.  Returns 0 when B or V is not positive. Host only. */
+size_t whiflash_entropy_workspace_bytes(int32_t B, int32_t V);
+
+/*
+ * WhiFlash-Entropy policy (WhiFlash paper, section 3.3.1 "Runtime-Informed
+ * Policy"): for each sequence b, the entropy in nats of the softmax of the
+ * logits row at its final accepted position,
+ *     H[b] = -sum_x p(x) log p(x),  p = softmax(row),
+ * and the decision choice[b] = 1 (EAGLE-3) if H[b] > tau, else 0 (DFlash).
+ *   logits: total_rows packed rows of V entries, row_stride apart (the rows the
+ *           verify entry points read).
+ *   The selected row of sequence b is row0[b] + pos[b], where row0 is a [B]
+ *   device array of each sequence's first row (e.g. the routed row_offsets),
+ *   or NULL meaning row0[b] = b * rows_per_seq; pos [B] is the position within
+ *   the sequence (the best_node output of the verify calls, or accept_len - 1
+ *   for a chain).  A negative pos or a row outside [0, total_rows) gives
+ *   H = NaN and choice 0.
+ *   entropy [B] float32 and choice [B] int32 are written.  The reduction runs
+ *   in float32 with a fixed merge order (bitwise reproducible).
+ * Precondition: the selected rows hold finite values.  B == 0 is a no-op.
+ */
+int32_t whiflash_route_entropy(const void* logits, int32_t dtype, int32_t total_rows, int32_t V,
+                               int64_t row_stride, int32_t B, const int32_t* row0,
+                               int32_t rows_per_seq, const int32_t* pos, float tau,
+                               float* entropy, int32_t* choice,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,8 @@ from .whiflash import (  # noqa: F401
     row_argmax,
     gelu,
     route,
+    entropy,
+    route_entropy,
     verify_chain,
     verify_tree,
     verify_routed,

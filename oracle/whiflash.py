@@ -103,6 +103,47 @@ def route(hidden, W1, b1, W2, b2, tau: float, dtype: str):
     return delta_al, choice
 
 
+def entropy(raw_row: np.ndarray, dtype: str) -> float:
+    """Entropy (nats) of the target's next-token distribution from one logits row.
+
+    [paper] §3.3.1 "Runtime-Informed Policy": H_t = -sum_x p(x) log p(x) over
+    the vocabulary at the final accepted position; under greedy decoding p is
+    the softmax of the logits (temperature 1).  Computed in float64 as
+    p = exp(x - max) / sum exp(x - max), with 0 log 0 = 0.  Precondition:
+    finite logits.
+    """
+    x = decode_logits(raw_row, dtype)
+    if not np.isfinite(x).all():
+        raise ValueError("entropy needs finite logits")
+    e = np.exp(x - x.max())
+    p = e / e.sum()
+    nz = p[p > 0]
+    return float(-(nz * np.log(nz)).sum())
+
+
+def route_entropy(raw: np.ndarray, dtype: str, rows, tau: float):
+    """WhiFlash-Entropy decision for each sequence from the row at its final accepted position.
+
+    [paper] §3.3.1, decision rule pi(H_t, tau_entropy): the autoregressive
+    drafter m_a (EAGLE-3, choice 1) when H_t > tau_entropy, else the diffusion
+    drafter m_d (DFlash, choice 0).  rows[b] is the packed row index of that
+    position; an index outside [0, total_rows) gives H = NaN and choice 0.
+    Returns (H float64 [B], choice int32 [B]).
+    """
+    raw = np.asarray(raw)
+    total = raw.shape[0]
+    B = len(rows)
+    H = np.full(B, np.nan)
+    choice = np.zeros(B, np.int32)
+    thr = float(np.float32(tau))
+    for b in range(B):
+        r = int(rows[b])
+        if 0 <= r < total:
+            H[b] = entropy(raw[r], dtype)
+            choice[b] = 1 if H[b] > thr else 0
+    return H, choice
+
+
 # ----------------------------------------------------------------------------- verify
 
 

@@ -111,3 +111,20 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "library_path", lambda: str(tmp_path / "libwhiflash.so"))
     with pytest.raises(_binding.WhiflashError):
         _binding.lib()
+
+
+def test_entropy_validation():
+    f = wf.whiflash_route_entropy
+    # (logits, dtype, total_rows, V, stride, B, row0, rows_per_seq, pos, tau, H, choice, ws, ws_bytes, stream)
+    ok = [ALIGNED, 1, 4992, V, V, 128, ALIGNED, 0, ALIGNED, 1.0, ALIGNED, ALIGNED, ALIGNED, 1 << 22, None]
+    bad = list(ok); bad[8] = None
+    assert f(*bad) == -1
+    bad = list(ok); bad[6] = None; bad[7] = -1
+    assert f(*bad) == -2
+    bad = list(ok); bad[13] = 16
+    assert f(*bad) == -5
+    bad = list(ok); bad[1] = 3
+    assert f(*bad) == -3
+    bad = list(ok); bad[5] = 0
+    assert f(*bad) == 0
+    assert wf.entropy_workspace_bytes(128, V) >= 128 * 16 and wf.entropy_workspace_bytes(0, V) == 0
