@@ -7,11 +7,14 @@ fallback: if the shared library is missing the import of the binding fails.
 
 Entry points (same names as the C ABI):
     route(hidden, W1, b1, W2, b2, tau)                    -> (delta_al, choice)
+    route_gather(hidden_rows, pos, W1, b1, W2, b2, tau, row0=None, rows_per_seq=0)
+                                                          -> (delta_al, choice)
     verify_chain(logits, draft)                           -> (accept_len, bonus, row_argmax)
     verify_tree(logits, parent, draft_ids, d2t)           -> (accept_len, bonus, best_node, row_argmax)
     verify_routed(logits, row_offsets, total_rows, choice, chain_draft, parent, draft_ids, d2t)
                                                           -> (accept_len, bonus, best_node, row_argmax)
     route_entropy(logits, pos, tau, row0=None, rows_per_seq=0)  -> (entropy, choice)
+    catchup_update(cur_choice, accept_len, next_choice, backlog)  -> (switch_flag, catchup_len)
 """
 
 from ._binding import (  # noqa: F401
@@ -25,11 +28,15 @@ from ._binding import (  # noqa: F401
     route_workspace_bytes,
     verify_workspace_bytes,
     route,
+    route_gather,
+    whiflash_route_gather,
     verify_chain,
     verify_tree,
     verify_routed,
     route_entropy,
     entropy_workspace_bytes,
+    catchup_update,
+    whiflash_catchup_update,
     whiflash_route_entropy,
     whiflash_route,
     whiflash_verify_chain,

@@ -31,6 +31,9 @@ _SIGNATURES = {
                                        _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_verify_tree": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
                                       _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "whiflash_route_gather": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p,
+                                       _c_p, _c_i32, _c_p, _c_p, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "whiflash_catchup_update": (_c_i32, [_c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "whiflash_entropy_workspace_bytes": (_c_sz, [_c_i32, _c_i32]),
     "whiflash_route_entropy": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_p, _c_i32,
                                         _c_p, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
@@ -92,6 +95,14 @@ def whiflash_verify_tree(*args):
 
 def whiflash_verify_routed(*args):
     return lib().whiflash_verify_routed(*args)
+
+
+def whiflash_route_gather(*args):
+    return lib().whiflash_route_gather(*args)
+
+
+def whiflash_catchup_update(*args):
+    return lib().whiflash_catchup_update(*args)
 
 
 def whiflash_route_entropy(*args):
@@ -199,6 +210,42 @@ def route(hidden, W1, b1, W2, b2, tau: float, *, delta_al=None, choice=None, wor
     _check(whiflash_route(_ptr(hidden), _dtype_code(hidden), B, d, _ptr(W1), _ptr(b1), m, _ptr(W2),
                           _ptr(b2), float(tau), _ptr(delta_al), _ptr(choice), _ptr(ws),
                           0 if ws is None else ws.numel() * ws.element_size(), _stream(hidden, stream)))
+    return delta_al, choice
+
+
+def route_gather(hidden_rows, pos, W1, b1, W2, b2, tau: float, *, row0=None, rows_per_seq: int = 0,
+                 delta_al=None, choice=None, workspace=None, stream=None):
+    """Neural router on the hidden state at each sequence's final accepted position.
+    hidden_rows [total_rows, d]; pos [B] int32; row0 [B] int32 or None with rows_per_seq."""
+    _device_tensor(hidden_rows, "hidden_rows")
+    _device_tensor(pos, "pos")
+    total_rows, d = hidden_rows.shape
+    B = pos.numel()
+    m = W1.shape[0]
+    for t, name in ((hidden_rows, "hidden_rows"), (W1, "W1"), (W2, "W2")):
+        _device_tensor(t, name)
+        if not t.is_contiguous() or t.dtype != hidden_rows.dtype:
+            raise TypeError(f"{name} must be contiguous with the dtype of hidden_rows")
+    if tuple(W1.shape) != (m, d) or W2.numel() != m:
+        raise ValueError("W1 must be [m, d] and W2 hold m elements")
+    _i32(pos, "pos", B)
+    if row0 is not None:
+        _i32(row0, "row0")
+        if row0.numel() < B:
+            raise ValueError("row0 must hold at least B entries")
+    dev = hidden_rows.device
+    if b1 is not None and (b1.dtype != torch.float32 or b1.numel() != m or not b1.is_contiguous()):
+        raise TypeError("b1 must be a contiguous float32 tensor of m elements")
+    if b2 is not None and not isinstance(b2, torch.Tensor):
+        b2 = torch.tensor([float(b2)], dtype=torch.float32, device=dev)
+    delta_al = torch.empty(B, dtype=torch.float32, device=dev) if delta_al is None else delta_al
+    choice = torch.empty(B, dtype=torch.int32, device=dev) if choice is None else choice
+    ws = _workspace(workspace, route_workspace_bytes(B, m), dev)
+    _check(whiflash_route_gather(_ptr(hidden_rows), _dtype_code(hidden_rows), total_rows, d, B,
+                                 _ptr(row0), rows_per_seq, _ptr(pos), _ptr(W1), _ptr(b1), m,
+                                 _ptr(W2), _ptr(b2), float(tau), _ptr(delta_al), _ptr(choice),
+                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                 _stream(hidden_rows, stream)))
     return delta_al, choice
 
 
@@ -317,3 +364,27 @@ def route_entropy(logits, pos, tau: float, *, row0=None, rows_per_seq: int = 0, 
                                   0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(logits, stream)))
     return entropy, choice
+
+
+def catchup_update(cur_choice, accept_len, next_choice, backlog, *, switch_flag=True,
+                   catchup_len=True, stream=None):
+    """Lazy catch-up bookkeeping; backlog [B, 2] int32 is updated in place.
+    Returns (switch_flag, catchup_len) (None where not requested)."""
+    B = cur_choice.numel()
+    _i32(cur_choice, "cur_choice", B)
+    _i32(accept_len, "accept_len", B)
+    _i32(next_choice, "next_choice", B)
+    _i32(backlog, "backlog", 2 * B)
+    dev = backlog.device
+    if switch_flag is True:
+        switch_flag = torch.empty(B, dtype=torch.int32, device=dev)
+    elif switch_flag is False:
+        switch_flag = None
+    if catchup_len is True:
+        catchup_len = torch.empty(B, dtype=torch.int32, device=dev)
+    elif catchup_len is False:
+        catchup_len = None
+    _check(whiflash_catchup_update(B, _ptr(cur_choice), _ptr(accept_len), _ptr(next_choice),
+                                   _ptr(backlog), _ptr(switch_flag), _ptr(catchup_len),
+                                   _stream(backlog, stream)))
+    return switch_flag, catchup_len

@@ -70,10 +70,14 @@ size_t whiflash_verify_workspace_bytes(int32_t total_rows, int32_t V) {
   return round_up(static_cast<size_t>(total_rows) * plan.splits * sizeof(wf::Partial), kWorkspaceAlign);
 }
 
-int32_t whiflash_route(const void* hidden, int32_t dtype, int32_t B, int32_t d, const void* W1,
-                       const float* b1, int32_t m, const void* W2, const float* b2, float tau,
-                       float* delta_al, int32_t* choice, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int32_t route_impl(const void* hidden, const wf::HiddenSel& sel, int32_t dtype, int32_t B,
+                   int32_t d, const void* W1, const float* b1, int32_t m, const void* W2,
+                   const float* b2, float tau, float* delta_al, int32_t* choice, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
   if (!valid_dtype(dtype)) return WF_ERR_DTYPE;
   if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
   if (B == 0) return WF_OK;
@@ -85,10 +89,41 @@ int32_t whiflash_route(const void* hidden, int32_t dtype, int32_t B, int32_t d, 
   if (s != WF_OK) return s;
   float* zp = static_cast<float*>(workspace);
   const wf::RouterPlan plan = wf::router_plan(dtype, B, d, m, hidden, W1);
-  if (wf::launch_router_stage1(plan, hidden, dtype, B, d, W1, m, zp, stream) != hipSuccess)
+  if (wf::launch_router_stage1(plan, hidden, sel, dtype, B, d, W1, m, zp, stream) != hipSuccess)
     return WF_ERR_LAUNCH;
-  return launch_status(wf::launch_router_finish(plan, dtype, zp, B, m, b1, W2, b2, tau, delta_al,
-                                                choice, stream));
+  return launch_status(wf::launch_router_finish(plan, sel, dtype, zp, B, m, b1, W2, b2, tau,
+                                                delta_al, choice, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t whiflash_route(const void* hidden, int32_t dtype, int32_t B, int32_t d, const void* W1,
+                       const float* b1, int32_t m, const void* W2, const float* b2, float tau,
+                       float* delta_al, int32_t* choice, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  const wf::HiddenSel direct{nullptr, nullptr, 0, 0};
+  return route_impl(hidden, direct, dtype, B, d, W1, b1, m, W2, b2, tau, delta_al, choice,
+                    workspace, workspace_bytes, stream);
+}
+
+int32_t whiflash_route_gather(const void* hidden_rows, int32_t dtype, int32_t total_rows,
+                              int32_t d, int32_t B, const int32_t* row0, int32_t rows_per_seq,
+                              const int32_t* pos, const void* W1, const float* b1, int32_t m,
+                              const void* W2, const float* b2, float tau, float* delta_al,
+                              int32_t* choice, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  if (total_rows < 0 || (row0 == nullptr && rows_per_seq < 0)) return WF_ERR_SHAPE;
+  if (B > 0 && pos == nullptr) return WF_ERR_NULL;
+  if (B > 0 && total_rows == 0 && hidden_rows == nullptr) {
+    // No rows at all: every sequence gets NaN / 0 from the finish kernel, but the
+    // stage-1 kernels still need a base pointer; any non-null value is never read.
+    hidden_rows = W1;
+  }
+  const wf::HiddenSel sel{row0, pos, rows_per_seq, total_rows};
+  return route_impl(hidden_rows, sel, dtype, B, d, W1, b1, m, W2, b2, tau, delta_al, choice,
+                    workspace, workspace_bytes, stream);
 }
 
 int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int32_t K, int32_t V,
@@ -163,6 +198,16 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
                                                   choice, K, chain_draft, N, parent, draft_ids, d2t,
                                                   Vd, accept_len, bonus, best_node, row_argmax,
                                                   stream));
+}
+
+int32_t whiflash_catchup_update(int32_t B, const int32_t* cur_choice, const int32_t* accept_len,
+                                const int32_t* next_choice, int32_t* backlog, int32_t* switch_flag,
+                                int32_t* catchup_len, hipStream_t stream) {
+  if (B < 0) return WF_ERR_SHAPE;
+  if (B == 0) return WF_OK;
+  if (!cur_choice || !accept_len || !next_choice || !backlog) return WF_ERR_NULL;
+  return launch_status(wf::launch_catchup(B, cur_choice, accept_len, next_choice, backlog,
+                                          switch_flag, catchup_len, stream));
 }
 
 size_t whiflash_entropy_workspace_bytes(int32_t B, int32_t V) {

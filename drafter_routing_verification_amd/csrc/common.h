@@ -29,6 +29,29 @@ struct SweepPlan {
 
 SweepPlan sweep_plan(int32_t rows, int32_t V);
 
+// Row of sequence b selected as row0[b] + pos[b] (row0 NULL: b * rows_per_seq),
+// or -1 when pos[b] < 0 or the row falls outside [0, total_rows).
+__device__ inline int64_t select_row(const int32_t* row0, int32_t rows_per_seq, const int32_t* pos,
+                                     int32_t total_rows, int b) {
+  const int p = pos[b];
+  const int64_t r =
+      (row0 ? static_cast<int64_t>(row0[b]) : static_cast<int64_t>(b) * rows_per_seq) + p;
+  return (p >= 0 && r >= 0 && r < total_rows) ? r : -1;
+}
+
+// Which hidden row feeds sequence b of the router: b itself (pos == NULL), or
+// the row selected by (row0, rows_per_seq, pos) among total_rows rows.
+struct HiddenSel {
+  const int32_t* row0;
+  const int32_t* pos;
+  int32_t rows_per_seq;
+  int32_t total_rows;
+};
+
+__device__ inline int64_t hidden_row(const HiddenSel& s, int b) {
+  return s.pos ? select_row(s.row0, s.rows_per_seq, s.pos, s.total_rows, b) : b;
+}
+
 hipError_t launch_sweep(const void* logits, int dtype, int64_t row_stride, int32_t rows, int32_t V,
                         SweepPlan plan, Partial* part, hipStream_t stream);
 
@@ -64,13 +87,14 @@ int32_t router_max_slices(int32_t B, int32_t m);
 RouterPlan router_plan(int dtype, int32_t B, int32_t d, int32_t m, const void* hidden,
                        const void* W1);
 
-hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, int dtype, int32_t B,
-                                int32_t d, const void* W1, int32_t m, float* zp,
-                                hipStream_t stream);
+hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, const HiddenSel& sel,
+                                int dtype, int32_t B, int32_t d, const void* W1, int32_t m,
+                                float* zp, hipStream_t stream);
 
-hipError_t launch_router_finish(const RouterPlan& plan, int dtype, const float* zp, int32_t B,
-                                int32_t m, const float* b1, const void* W2, const float* b2,
-                                float tau, float* delta_al, int32_t* choice, hipStream_t stream);
+hipError_t launch_router_finish(const RouterPlan& plan, const HiddenSel& sel, int dtype,
+                                const float* zp, int32_t B, int32_t m, const float* b1,
+                                const void* W2, const float* b2, float tau, float* delta_al,
+                                int32_t* choice, hipStream_t stream);
 
 // Entropy policy: partials float4 {m, S, U, -} per (sequence, chunk), then one
 // finish kernel.  Workspace: B * splits * 16 bytes.
@@ -79,5 +103,10 @@ hipError_t launch_entropy(const void* logits, int dtype, int64_t row_stride, int
                           int32_t V, int32_t B, const int32_t* row0, int32_t rows_per_seq,
                           const int32_t* pos, float tau, float* entropy, int32_t* choice,
                           void* workspace, hipStream_t stream);
+
+// Lazy catch-up bookkeeping, one thread per sequence.
+hipError_t launch_catchup(int32_t B, const int32_t* cur, const int32_t* accept_len,
+                          const int32_t* nxt, int32_t* backlog, int32_t* switch_flag,
+                          int32_t* catchup_len, hipStream_t stream);
 
 }  // namespace wf

@@ -43,13 +43,6 @@ __device__ inline Ent shfl_xor(const Ent& e, int off) {
   return Ent{__shfl_xor(e.m, off), __shfl_xor(e.S, off), __shfl_xor(e.U, off)};
 }
 
-__device__ inline int64_t selected_row(int b, const int32_t* row0, int rows_per_seq,
-                                       const int32_t* pos, int total_rows) {
-  const int p = pos[b];
-  const int64_t r = (row0 ? static_cast<int64_t>(row0[b]) : static_cast<int64_t>(b) * rows_per_seq) + p;
-  return (p >= 0 && r >= 0 && r < total_rows) ? r : -1;
-}
-
 template <int DT>
 __global__ __launch_bounds__(kThreads) void entropy_partial_kernel(
     const unsigned char* __restrict__ logits, int64_t row_bytes, int total_rows, int V,
@@ -59,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void entropy_partial_kernel(
   const int blk = blockIdx.x;
   const int b = blk / splits;
   const int c = blk - b * splits;
-  const int64_t row = selected_row(b, row0, rows_per_seq, pos, total_rows);
+  const int64_t row = select_row(row0, rows_per_seq, pos, total_rows, b);
   const int tid = threadIdx.x;
   Ent acc{-INFINITY, 0.f, 0.f};
   if (row >= 0) {
@@ -138,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void entropy_finish_kernel(
     ent_merge(acc, o);
   }
   if (lane == 0) {
-    const bool valid = selected_row(b, row0, rows_per_seq, pos, total_rows) >= 0 && acc.S > 0.f;
+    const bool valid = select_row(row0, rows_per_seq, pos, total_rows, b) >= 0 && acc.S > 0.f;
     const float H = valid ? kLn2 * (__builtin_amdgcn_logf(acc.S) - acc.U / acc.S) : NAN;
     entropy[b] = H;
     choice[b] = (valid && H > tau) ? 1 : 0;

@@ -66,13 +66,17 @@ __device__ inline float dot16(u32x4 a, u32x4 b, float acc) {
 // each lane reads 16-byte vectors, kGemvUnroll of them in flight.
 template <int DT, int NB, bool VEC>
 __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
-    const void* __restrict__ hidden, int B, int d, const void* __restrict__ W1, int m,
+    const void* __restrict__ hidden, HiddenSel sel, int B, int d, const void* __restrict__ W1, int m,
     float* __restrict__ zp) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int b0 = blockIdx.y * NB;
   if (j >= m) return;
   const int nb = min(NB, B - b0);
+  // Hidden row of each of this wave's sequences (-1: no valid row, dot stays 0).
+  int64_t hrow[NB];
+#pragma unroll
+  for (int q = 0; q < NB; ++q) hrow[q] = q < nb ? hidden_row(sel, b0 + q) : -1;
   float acc[NB];
 #pragma unroll
   for (int q = 0; q < NB; ++q) acc[q] = 0.f;
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
     constexpr int kPer = DT == WF_BF16 ? 8 : 4;
     const int nv = d / kPer;
     const u32x4* wr = reinterpret_cast<const u32x4*>(W1) + static_cast<int64_t>(j) * nv;
-    const u32x4* hr = reinterpret_cast<const u32x4*>(hidden) + static_cast<int64_t>(b0) * nv;
+    const u32x4* hb = reinterpret_cast<const u32x4*>(hidden);
     int v = lane;
     for (; v + (kGemvUnroll - 1) * 64 < nv; v += kGemvUnroll * 64) {
       u32x4 w[kGemvUnroll];
@@ -88,10 +92,11 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
       for (int u = 0; u < kGemvUnroll; ++u) w[u] = wr[v + u * 64];
 #pragma unroll
       for (int q = 0; q < NB; ++q) {
-        if (q < nb) {
+        if (hrow[q] >= 0) {
+          const u32x4* hr = hb + hrow[q] * nv;
           u32x4 h[kGemvUnroll];
 #pragma unroll
-          for (int u = 0; u < kGemvUnroll; ++u) h[u] = hr[static_cast<int64_t>(q) * nv + v + u * 64];
+          for (int u = 0; u < kGemvUnroll; ++u) h[u] = hr[v + u * 64];
 #pragma unroll
           for (int u = 0; u < kGemvUnroll; ++u) acc[q] = dot16<DT>(w[u], h[u], acc[q]);
         }
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
       const u32x4 w = wr[v];
 #pragma unroll
       for (int q = 0; q < NB; ++q)
-        if (q < nb) acc[q] = dot16<DT>(w, hr[static_cast<int64_t>(q) * nv + v], acc[q]);
+        if (hrow[q] >= 0) acc[q] = dot16<DT>(w, hb[hrow[q] * nv + v], acc[q]);
     }
   } else {
     const int64_t wrow = static_cast<int64_t>(j) * d;
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
       const float w = load_elem<DT>(W1, wrow + k);
 #pragma unroll
       for (int q = 0; q < NB; ++q)
-        if (q < nb) acc[q] = fmaf(w, load_elem<DT>(hidden, static_cast<int64_t>(b0 + q) * d + k), acc[q]);
+        if (hrow[q] >= 0) acc[q] = fmaf(w, load_elem<DT>(hidden, hrow[q] * d + k), acc[q]);
     }
   }
 #pragma unroll
@@ -131,8 +136,8 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
 // at 8 * (l / 16); the accumulator of lane l holds rows 4 * (l / 16) + i,
 // i = 0..3, of column l % 16.
 __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
-    const unsigned short* __restrict__ hidden, int B, int d, const unsigned short* __restrict__ W1,
-    int m, int kslice, float* __restrict__ zp) {
+    const unsigned short* __restrict__ hidden, HiddenSel sel, int B, int d,
+    const unsigned short* __restrict__ W1, int m, int kslice, float* __restrict__ zp) {
   __shared__ __attribute__((aligned(16))) unsigned short stage[kStageRows * kStageStride];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j0 = blockIdx.x * kMfmaTileJ, bb0 = blockIdx.y * kMfmaTileB, slice = blockIdx.z;
@@ -142,6 +147,19 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
   // Rows this thread stages: row = i * 16 + (tid >> 4), piece column tid & 15.
   const int prow = tid >> 4, pcol = (tid & 15) * 8;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  // Source row of each piece this thread stages (nullptr: zeros).
+  const unsigned short* src[kPiecesPerThread];
+#pragma unroll
+  for (int i = 0; i < kPiecesPerThread; ++i) {
+    const int row = i * 16 + prow;
+    src[i] = nullptr;
+    if (row < kMfmaTileJ) {
+      if (j0 + row < m) src[i] = W1 + static_cast<int64_t>(j0 + row) * d;
+    } else if (bb0 + row - kMfmaTileJ < B) {
+      const int64_t h = hidden_row(sel, bb0 + row - kMfmaTileJ);
+      if (h >= 0) src[i] = hidden + h * d;
+    }
+  }
   const int nchunks = (k1 - k0 + kChunk - 1) / kChunk;
   for (int c0 = 0; c0 < nchunks; c0 += kChunksInFlight) {
     u32x4 buf[kChunksInFlight][kPiecesPerThread];
@@ -149,16 +167,10 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
     for (int c = 0; c < kChunksInFlight; ++c) {
 #pragma unroll
       for (int i = 0; i < kPiecesPerThread; ++i) {
-        const int row = i * 16 + prow;
         const int k = k0 + (c0 + c) * kChunk + pcol;
-        const unsigned short* src = nullptr;
-        if (row < kMfmaTileJ) {
-          if (j0 + row < m) src = W1 + static_cast<int64_t>(j0 + row) * d;
-        } else if (bb0 + row - kMfmaTileJ < B) {
-          src = hidden + static_cast<int64_t>(bb0 + row - kMfmaTileJ) * d;
-        }
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (src != nullptr && c0 + c < nchunks && k < k1) v = *reinterpret_cast<const u32x4*>(src + k);
+        if (src[i] != nullptr && c0 + c < nchunks && k < k1)
+          v = *reinterpret_cast<const u32x4*>(src[i] + k);
         buf[c][i] = v;
       }
     }
@@ -208,7 +220,7 @@ constexpr int kFinishPer = 4;
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void router_finish_kernel(
-    const float* __restrict__ zp, int KS, int B, int m, const float* __restrict__ b1,
+    const float* __restrict__ zp, HiddenSel sel, int KS, int B, int m, const float* __restrict__ b1,
     const void* __restrict__ W2, const float* __restrict__ b2, float tau,
     float* __restrict__ delta_al, int32_t* __restrict__ choice) {
   __shared__ float red[kWaves];
@@ -248,6 +260,7 @@ __global__ __launch_bounds__(kThreads) void router_finish_kernel(
     float v = red[0];
     for (int w = 1; w < kWaves; ++w) v += red[w];
     v += b2 ? *b2 : 0.f;
+    if (hidden_row(sel, b) < 0) v = NAN;  // no hidden row for this sequence
     delta_al[b] = v;
     choice[b] = v > tau ? 1 : 0;
   }
@@ -282,30 +295,30 @@ int32_t router_max_slices(int32_t B, int32_t m) {
 }
 
 template <int DT, int NB, bool VEC>
-static void gemv_launch(dim3 grid, hipStream_t stream, const void* hidden, int32_t B, int32_t d,
-                        const void* W1, int32_t m, float* zp) {
-  hipLaunchKernelGGL((router_gemv_kernel<DT, NB, VEC>), grid, dim3(kThreads), 0, stream, hidden, B,
-                     d, W1, m, zp);
+static void gemv_launch(dim3 grid, hipStream_t stream, const void* hidden, const HiddenSel& sel,
+                        int32_t B, int32_t d, const void* W1, int32_t m, float* zp) {
+  hipLaunchKernelGGL((router_gemv_kernel<DT, NB, VEC>), grid, dim3(kThreads), 0, stream, hidden, sel,
+                     B, d, W1, m, zp);
 }
 
 template <int DT, bool VEC>
-static void gemv_dispatch(const void* hidden, int32_t B, int32_t d, const void* W1, int32_t m,
-                          float* zp, hipStream_t stream) {
+static void gemv_dispatch(const void* hidden, const HiddenSel& sel, int32_t B, int32_t d,
+                          const void* W1, int32_t m, float* zp, hipStream_t stream) {
   const unsigned gx = (m + kWaves - 1) / kWaves;
-  if (B == 1) gemv_launch<DT, 1, VEC>(dim3(gx, 1), stream, hidden, B, d, W1, m, zp);
-  else if (B <= 2) gemv_launch<DT, 2, VEC>(dim3(gx, 1), stream, hidden, B, d, W1, m, zp);
-  else if (B <= 4) gemv_launch<DT, 4, VEC>(dim3(gx, 1), stream, hidden, B, d, W1, m, zp);
-  else gemv_launch<DT, 8, VEC>(dim3(gx, (B + 7) / 8), stream, hidden, B, d, W1, m, zp);
+  if (B == 1) gemv_launch<DT, 1, VEC>(dim3(gx, 1), stream, hidden, sel, B, d, W1, m, zp);
+  else if (B <= 2) gemv_launch<DT, 2, VEC>(dim3(gx, 1), stream, hidden, sel, B, d, W1, m, zp);
+  else if (B <= 4) gemv_launch<DT, 4, VEC>(dim3(gx, 1), stream, hidden, sel, B, d, W1, m, zp);
+  else gemv_launch<DT, 8, VEC>(dim3(gx, (B + 7) / 8), stream, hidden, sel, B, d, W1, m, zp);
 }
 
-hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, int dtype, int32_t B,
-                                int32_t d, const void* W1, int32_t m, float* zp,
-                                hipStream_t stream) {
+hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, const HiddenSel& sel,
+                                int dtype, int32_t B, int32_t d, const void* W1, int32_t m,
+                                float* zp, hipStream_t stream) {
   if (plan.mfma) {
     const dim3 grid((m + kMfmaTileJ - 1) / kMfmaTileJ, (B + kMfmaTileB - 1) / kMfmaTileB,
                     plan.slices);
     hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(kThreads), 0, stream,
-                       static_cast<const unsigned short*>(hidden), B, d,
+                       static_cast<const unsigned short*>(hidden), sel, B, d,
                        static_cast<const unsigned short*>(W1), m, plan.kslice, zp);
     return hipGetLastError();
   }
@@ -313,23 +326,24 @@ hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, int 
   const bool vec = (reinterpret_cast<uintptr_t>(hidden) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(W1) % 16 == 0) && (d % per == 0);
   if (dtype == WF_BF16) {
-    if (vec) gemv_dispatch<WF_BF16, true>(hidden, B, d, W1, m, zp, stream);
-    else gemv_dispatch<WF_BF16, false>(hidden, B, d, W1, m, zp, stream);
+    if (vec) gemv_dispatch<WF_BF16, true>(hidden, sel, B, d, W1, m, zp, stream);
+    else gemv_dispatch<WF_BF16, false>(hidden, sel, B, d, W1, m, zp, stream);
   } else {
-    if (vec) gemv_dispatch<WF_F32, true>(hidden, B, d, W1, m, zp, stream);
-    else gemv_dispatch<WF_F32, false>(hidden, B, d, W1, m, zp, stream);
+    if (vec) gemv_dispatch<WF_F32, true>(hidden, sel, B, d, W1, m, zp, stream);
+    else gemv_dispatch<WF_F32, false>(hidden, sel, B, d, W1, m, zp, stream);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_router_finish(const RouterPlan& plan, int dtype, const float* zp, int32_t B,
-                                int32_t m, const float* b1, const void* W2, const float* b2,
-                                float tau, float* delta_al, int32_t* choice, hipStream_t stream) {
+hipError_t launch_router_finish(const RouterPlan& plan, const HiddenSel& sel, int dtype,
+                                const float* zp, int32_t B, int32_t m, const float* b1,
+                                const void* W2, const float* b2, float tau, float* delta_al,
+                                int32_t* choice, hipStream_t stream) {
   if (dtype == WF_BF16)
-    hipLaunchKernelGGL(router_finish_kernel<WF_BF16>, dim3(B), dim3(kThreads), 0, stream, zp,
+    hipLaunchKernelGGL(router_finish_kernel<WF_BF16>, dim3(B), dim3(kThreads), 0, stream, zp, sel,
                        plan.slices, B, m, b1, W2, b2, tau, delta_al, choice);
   else
-    hipLaunchKernelGGL(router_finish_kernel<WF_F32>, dim3(B), dim3(kThreads), 0, stream, zp,
+    hipLaunchKernelGGL(router_finish_kernel<WF_F32>, dim3(B), dim3(kThreads), 0, stream, zp, sel,
                        plan.slices, B, m, b1, W2, b2, tau, delta_al, choice);
   return hipGetLastError();
 }

@@ -94,6 +94,27 @@ int32_t whiflash_route(const void* hidden, int32_t dtype, int32_t B, int32_t d,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The same router fed from the hidden state at each sequence's final accepted
+ * position (WhiFlash paper, section 3.3.2: the policy takes the final-layer
+ * hidden state at the current decoding step; section 3.3.1: the final
+ * accepted position).  hidden_rows [total_rows, d] holds the target's hidden
+ * states for every verified row (the rows the verify calls read); sequence b
+ * uses row row0[b] + pos[b], where row0 [B] is each sequence's first row (e.g.
+ * the routed row_offsets) or NULL meaning b * rows_per_seq, and pos [B] is the
+ * accepted position within the sequence (best_node from the verify calls, or
+ * accept_len - 1 for a chain).  A negative pos or a row outside
+ * [0, total_rows) gives delta_al = NaN and choice 0.  Other arguments, the
+ * workspace (whiflash_route_workspace_bytes(B, m)) and the arithmetic are
+ * those of whiflash_route.
+ */
+int32_t whiflash_route_gather(const void* hidden_rows, int32_t dtype, int32_t total_rows,
+                              int32_t d, int32_t B, const int32_t* row0, int32_t rows_per_seq,
+                              const int32_t* pos, const void* W1, const float* b1, int32_t m,
+                              const void* W2, const float* b2, float tau, float* delta_al,
+                              int32_t* choice, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * Greedy verification of DFlash blocks (WhiFlash paper, section 3.2: the
  * drafted block is verified in parallel and decoding continues from the last
  * accepted token; section 4 "Metrics": AL counts tokens per round).
@@ -168,6 +189,25 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
                                int32_t* accept_len, int32_t* bonus, int32_t* best_node,
                                int32_t* row_argmax,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Lazy catch-up bookkeeping (WhiFlash paper, section 3.4 "Lazy Catch-up": the
+ * inactive drafter defers its KV-cache updates; the tokens accepted while it
+ * is inactive are its backlog, prefilled in one batch when a switch to it is
+ * committed).  Per sequence b, after a round verified with drafter
+ * cur_choice[b] (0 DFlash, 1 EAGLE-3) that accepted accept_len[b] tokens, and
+ * with next_choice[b] chosen for the next round:
+ *     backlog[b][1 - cur] += accept_len[b]           (if accept_len[b] > 0)
+ *     if next != cur: catchup_len[b] = backlog[b][next]; backlog[b][next] = 0;
+ *                     switch_flag[b] = 1
+ *     else:           catchup_len[b] = 0; switch_flag[b] = 0
+ * backlog [B, 2] int32 is updated in place (start from zeros).  A choice
+ * outside {0, 1} leaves the sequence unchanged with no switch.
+ * switch_flag [B] and catchup_len [B] may be NULL.  No workspace.
+ */
+int32_t whiflash_catchup_update(int32_t B, const int32_t* cur_choice, const int32_t* accept_len,
+                                const int32_t* next_choice, int32_t* backlog, int32_t* switch_flag,
+                                int32_t* catchup_len, hipStream_t stream);
 
 /* Workspace bytes whiflash_route_entropy needs for B sequences and rows of V
  * entries.  Returns 0 when B or V is not positive. Host only. */

@@ -18,11 +18,13 @@ from .whiflash import (  # noqa: F401
     row_argmax,
     gelu,
     route,
+    route_gather,
     entropy,
     route_entropy,
     verify_chain,
     verify_tree,
     verify_routed,
+    catchup_update,
     MALFORMED_AL,
     MALFORMED_BONUS,
 )

@@ -103,6 +103,28 @@ def route(hidden, W1, b1, W2, b2, tau: float, dtype: str):
     return delta_al, choice
 
 
+def route_gather(hidden_rows, rows, W1, b1, W2, b2, tau: float, dtype: str):
+    """The neural router fed from the hidden state at each sequence's final accepted position.
+
+    [paper] §3.3.2: the policy takes the target's final-layer hidden state at
+    the current decoding step; with speculative decoding that is the state at
+    the final accepted position (§3.3.1 uses the same position).  rows[b] is
+    the packed row of that position; an index outside [0, total_rows) gives
+    Delta-AL = NaN and choice 0.  Returns (delta_al float64 [B], choice int32 [B]).
+    """
+    hidden_rows = np.asarray(hidden_rows)
+    rows = np.asarray(rows, np.int64)
+    total = hidden_rows.shape[0]
+    B = rows.shape[0]
+    dal = np.full(B, np.nan)
+    choice = np.zeros(B, np.int32)
+    ok = (rows >= 0) & (rows < total)
+    if ok.any():
+        d_ok, c_ok = route(hidden_rows[rows[ok]], W1, b1, W2, b2, tau, dtype)
+        dal[ok], choice[ok] = d_ok, c_ok
+    return dal, choice
+
+
 def entropy(raw_row: np.ndarray, dtype: str) -> float:
     """Entropy (nats) of the target's next-token distribution from one logits row.
 
@@ -252,3 +274,37 @@ def verify_routed(t_rows: np.ndarray, offsets: np.ndarray, choice: np.ndarray, K
                                     np.asarray(draft_ids[b])[None, :], d2t, V)
             al[b], bonus[b], best[b] = a[0], bo[0], be[0]
     return al, bonus, best
+
+
+# ----------------------------------------------------------------------------- lazy catch-up
+
+
+def catchup_update(cur, accept_len, nxt, backlog):
+    """Backlog bookkeeping of lazy catch-up for one round.
+
+    [paper] §3.4 "Lazy Catch-up": the inactive drafter's KV cache is not
+    updated; tokens accepted while a drafter is inactive are its backlog, and
+    when a switch to it is committed it prefills that backlog in one batch.
+    Per sequence: this round's accepted tokens are added to the backlog of the
+    drafter that was not used (1 - cur); if the next round's drafter differs
+    (a switch), the incoming drafter's backlog is its catch-up length and is
+    reset to 0.  cur or nxt outside {0, 1} (e.g. a malformed sequence) leaves
+    the sequence unchanged with no switch.
+    backlog: int [B, 2] (column 0 DFlash, column 1 EAGLE-3), not modified.
+    Returns (new_backlog [B, 2], switch [B], catchup [B]) int32.
+    """
+    cur = np.asarray(cur)
+    B = cur.shape[0]
+    out = np.array(backlog, dtype=np.int64).reshape(B, 2)
+    switch = np.zeros(B, np.int32)
+    catchup = np.zeros(B, np.int32)
+    for b in range(B):
+        c, n, a = int(cur[b]), int(nxt[b]), int(accept_len[b])
+        if c not in (0, 1) or n not in (0, 1):
+            continue
+        out[b, 1 - c] += max(a, 0)
+        if n != c:
+            switch[b] = 1
+            catchup[b] = out[b, n]
+            out[b, n] = 0
+    return out.astype(np.int32), switch, catchup

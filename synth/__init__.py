@@ -22,4 +22,5 @@ from .workloads import (  # noqa: F401
     make_d2t,
     make_config,
     routed_calibration,
+    make_hidden_rows,
 )

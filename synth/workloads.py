@@ -330,3 +330,9 @@ def make_config(idx: int, rnd: int = 0, logits: bool = True, V: int = V_QWEN3):
                               VD_EAGLE3, c["dtype"], 0.8, 0.7, rnd, logits)
     batch.router = router
     return batch, router
+
+
+def make_hidden_rows(seed: int, rows: int, d: int = D_QWEN3, dtype: str = "bf16") -> np.ndarray:
+    """Final hidden states for every verified row: N(0, 1), one seeded stream."""
+    x = _rng(seed, _S_HIDDEN, 1_000_003).standard_normal((rows, d), dtype=np.float32)
+    return _materialise(x, dtype)

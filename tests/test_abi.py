@@ -128,3 +128,23 @@ def test_entropy_validation():
     bad = list(ok); bad[5] = 0
     assert f(*bad) == 0
     assert wf.entropy_workspace_bytes(128, V) >= 128 * 16 and wf.entropy_workspace_bytes(0, V) == 0
+
+
+def test_catchup_validation():
+    f = wf.whiflash_catchup_update
+    assert f(4, None, ALIGNED, ALIGNED, ALIGNED, None, None, None) == -1
+    assert f(-1, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, None, None) == -2
+    assert f(0, None, None, None, None, None, None, None) == 0
+
+
+def test_route_gather_validation():
+    f = wf.whiflash_route_gather
+    # (hidden_rows, dtype, total_rows, d, B, row0, rps, pos, W1, b1, m, W2, b2, tau, dal, ch, ws, ws_bytes, s)
+    ok = [ALIGNED, 1, 4992, 2560, 128, ALIGNED, 0, ALIGNED, ALIGNED, None, 1024, ALIGNED, None, 1.0,
+          ALIGNED, ALIGNED, ALIGNED, 1 << 26, None]
+    bad = list(ok); bad[7] = None
+    assert f(*bad) == -1
+    bad = list(ok); bad[5] = None; bad[6] = -3
+    assert f(*bad) == -2
+    bad = list(ok); bad[17] = 64
+    assert f(*bad) == -5

@@ -112,3 +112,14 @@ def test_bf16_rounding_is_nearest_even():
     x[:4] = [1.00390625, 1.01171875, -1.00390625, 3.0e38]   # exact halfway cases + large
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(f32_to_bf16_bits(x), ref)
+
+
+def test_route_gather_selects_rows_and_flags_invalid():
+    from oracle import route_gather
+    r = make_router_inputs(11, B=9, d=40, m=12, dtype="f32")
+    rows = np.array([3, 0, 8, -1, 9, 3], np.int64)
+    dal, ch = route_gather(r.hidden, rows, r.W1, r.b1, r.W2, np.float32(0.1), 0.0, "f32")
+    full, fch = route(r.hidden, r.W1, r.b1, r.W2, np.float32(0.1), 0.0, "f32")
+    assert dal[0] == full[3] and dal[1] == full[0] and dal[2] == full[8] and dal[5] == full[3]
+    assert np.isnan(dal[3]) and np.isnan(dal[4]) and ch[3] == 0 and ch[4] == 0
+    assert ch[0] == fch[3]
