@@ -93,3 +93,29 @@ def test_routed_bf16():
 def test_sweep_bf16(rnd):
     al = _chain(4, rnd)
     assert 4.0 < al.mean() < 5.8
+
+
+# Llama-3.1-8B shapes: DFlash block 10 (paper, Table 7), hidden 4096 and router width 512
+# (the 2.10M router parameters of the paper's Table 6 = 4096*512 + 512 + 512 + 1).  The pages
+# give no vocabulary size for this model; 128,256 (its tokenizer's) is used.
+LLAMA_V, LLAMA_D, LLAMA_M, LLAMA_K = 128256, 4096, 512, 10
+
+
+def test_llama_shapes_route_chain_tree():
+    from synth import make_chain_batch, make_router_inputs, make_tree_batch
+    print("llama shapes", flush=True)
+    r = make_router_inputs(81, 64, LLAMA_D, LLAMA_M, "bf16")
+    _route(r)
+    cb = make_chain_batch(82, 64, LLAMA_K, LLAMA_V, "bf16")
+    al, bo, rows = [host(x) for x in wf.verify_chain(dev(cb.logits), dev(cb.draft))]
+    t = oracle.row_argmax(cb.logits, "bf16")
+    e_al, e_bo = oracle.verify_chain(t.reshape(64, LLAMA_K + 1), cb.draft)
+    assert np.array_equal(rows, t) and np.array_equal(al, e_al) and np.array_equal(bo, e_bo)
+    assert al.max() <= LLAMA_K + 1
+    tb = make_tree_batch(83, 8, 61, LLAMA_V, 32000, "bf16")
+    out = [host(x) for x in wf.verify_tree(dev(tb.logits), dev(tb.parent), dev(tb.draft_ids),
+                                           dev(tb.d2t))]
+    t = oracle.row_argmax(tb.logits, "bf16")
+    e = oracle.verify_tree(t.reshape(8, 61), tb.parent, tb.draft_ids, tb.d2t, LLAMA_V)
+    assert np.array_equal(out[3], t)
+    assert all(np.array_equal(a, b) for a, b in zip(out[:3], e))
