@@ -44,6 +44,9 @@ def _parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", choices=["routed", "sweep"], default="routed")
     p.add_argument("--pool", type=int, default=4, help="distinct rounds resident in HBM (sweep)")
+    p.add_argument("--mode", choices=["fused", "separate"], default="fused",
+                   help="routed workload: whiflash_round_routed, or whiflash_route then "
+                        "whiflash_verify_routed")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -103,6 +106,8 @@ class Routed:
         self.rws = torch.empty(wf.route_workspace_bytes(B, r.m), dtype=torch.uint8, device=dev)
         self.vws = torch.empty(wf.verify_workspace_bytes(self.rows, self.V), dtype=torch.uint8,
                                device=dev)
+        self.fws = torch.empty(wf.round_workspace_bytes(B, r.m, self.rows, self.V),
+                               dtype=torch.uint8, device=dev)
         self.wf = wf
         self.setup_s = time.time() - t0
         esz = 2
@@ -121,6 +126,14 @@ class Routed:
                               self.parent, self.draft_ids, self.d2t, row_argmax=False,
                               accept_len=self.al, bonus=self.bonus, best_node=self.best,
                               workspace=self.vws)
+
+    def fused_step(self, i):
+        r = self.router
+        self.wf.round_routed(self.hidden, self.W1, self.b1, self.W2, self.b2, r.tau, self.logits,
+                             self.offsets, self.rows, self.chain_draft, self.parent,
+                             self.draft_ids, self.d2t, row_argmax=False, delta_al=self.dal,
+                             choice=self.choice, accept_len=self.al, bonus=self.bonus,
+                             best_node=self.best, workspace=self.fws)
 
     def check(self):
         al = self.al.cpu().numpy()
@@ -250,9 +263,17 @@ def main():
     print(f"# workload {work.name}: inputs resident in HBM ({work.setup_s:.1f} s setup)",
           file=sys.stderr, flush=True)
 
+    fused = args.mode == "fused" and hasattr(work, "fused_step")
+
+    def step(i):
+        if fused:
+            work.fused_step(i)
+        else:
+            work.route(i)
+            work.verify(i)
+
     for i in range(args.warmup):
-        work.route(i)
-        work.verify(i)
+        step(i)
     torch.cuda.synchronize()
     mean_al = work.check()
 
@@ -262,8 +283,7 @@ def main():
     w0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        work.route(i)
-        work.verify(i)
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -302,7 +322,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; planted-argmax logits, random trees, random router weights)",
-        "config": {"workload": work.name, "batch": work.B, "logits_rows": work.rows,
+        "config": {"workload": work.name, "mode": "whiflash_round_routed" if fused else
+                   "whiflash_route + whiflash_verify_*", "batch": work.B, "logits_rows": work.rows,
                    "vocab": work.V, "hidden": 2560, "router_width": 1024,
                    "logits_bytes_per_round": work.logits_bytes,
                    "bytes_per_round": work.step_bytes},

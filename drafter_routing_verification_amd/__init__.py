@@ -15,6 +15,9 @@ Entry points (same names as the C ABI):
                                                           -> (accept_len, bonus, best_node, row_argmax)
     route_entropy(logits, pos, tau, row0=None, rows_per_seq=0)  -> (entropy, choice)
     catchup_update(cur_choice, accept_len, next_choice, backlog)  -> (switch_flag, catchup_len)
+    round_routed(hidden, W1, b1, W2, b2, tau, logits, row_offsets, total_rows, chain_draft,
+                 parent, draft_ids, d2t)   route + verify_routed fused
+                 -> (delta_al, choice, accept_len, bonus, best_node, row_argmax)
 """
 
 from ._binding import (  # noqa: F401
@@ -37,6 +40,9 @@ from ._binding import (  # noqa: F401
     entropy_workspace_bytes,
     catchup_update,
     whiflash_catchup_update,
+    round_routed,
+    round_workspace_bytes,
+    whiflash_round_routed,
     whiflash_route_entropy,
     whiflash_route,
     whiflash_verify_chain,

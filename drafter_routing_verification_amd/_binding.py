@@ -33,6 +33,11 @@ _SIGNATURES = {
                                       _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_route_gather": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p,
                                        _c_p, _c_i32, _c_p, _c_p, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "whiflash_round_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "whiflash_round_routed": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_f,
+                                       _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_p,
+                                       _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_i32,
+                                       _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_catchup_update": (_c_i32, [_c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "whiflash_entropy_workspace_bytes": (_c_sz, [_c_i32, _c_i32]),
     "whiflash_route_entropy": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_p, _c_i32,
@@ -99,6 +104,14 @@ def whiflash_verify_routed(*args):
 
 def whiflash_route_gather(*args):
     return lib().whiflash_route_gather(*args)
+
+
+def whiflash_round_routed(*args):
+    return lib().whiflash_round_routed(*args)
+
+
+def round_workspace_bytes(B: int, m: int, total_rows: int, V: int) -> int:
+    return int(lib().whiflash_round_workspace_bytes(B, m, total_rows, V))
 
 
 def whiflash_catchup_update(*args):
@@ -388,3 +401,55 @@ def catchup_update(cur_choice, accept_len, next_choice, backlog, *, switch_flag=
                                    _ptr(backlog), _ptr(switch_flag), _ptr(catchup_len),
                                    _stream(backlog, stream)))
     return switch_flag, catchup_len
+
+
+def round_routed(hidden, W1, b1, W2, b2, tau: float, logits, row_offsets, total_rows: int,
+                 chain_draft, parent, draft_ids, d2t, *, row_argmax=True, delta_al=None,
+                 choice=None, accept_len=None, bonus=None, best_node=None, workspace=None,
+                 stream=None):
+    """route + verify_routed in one call (three launches).  Returns
+    (delta_al, choice, accept_len, bonus, best_node, row_argmax)."""
+    _device_tensor(hidden, "hidden")
+    B, d = hidden.shape
+    m = W1.shape[0]
+    for t, name in ((hidden, "hidden"), (W1, "W1"), (W2, "W2")):
+        _device_tensor(t, name)
+        if not t.is_contiguous() or t.dtype != hidden.dtype:
+            raise TypeError(f"{name} must be contiguous with the dtype of hidden")
+    if tuple(W1.shape) != (m, d) or W2.numel() != m:
+        raise ValueError("W1 must be [m, d] and W2 hold m elements")
+    dev = hidden.device
+    if b1 is not None and (b1.dtype != torch.float32 or b1.numel() != m or not b1.is_contiguous()):
+        raise TypeError("b1 must be a contiguous float32 tensor of m elements")
+    if b2 is not None and not isinstance(b2, torch.Tensor):
+        b2 = torch.tensor([float(b2)], dtype=torch.float32, device=dev)
+    if logits.dim() != 2:
+        raise ValueError("routed logits must be [total_rows, V]")
+    V, stride = _rows_view(logits, total_rows)
+    _i32(row_offsets, "row_offsets", B + 1)
+    K = chain_draft.shape[1]
+    N = parent.shape[1]
+    _i32(chain_draft, "chain_draft", B * K)
+    _i32(parent, "parent", B * N)
+    _i32(draft_ids, "draft_ids", B * N)
+    _i32(d2t, "d2t")
+    new = lambda dt: torch.empty(B, dtype=dt, device=dev)
+    delta_al = new(torch.float32) if delta_al is None else delta_al
+    choice = new(torch.int32) if choice is None else choice
+    accept_len = new(torch.int32) if accept_len is None else accept_len
+    bonus = new(torch.int32) if bonus is None else bonus
+    best_node = new(torch.int32) if best_node is None else best_node
+    if row_argmax is True:
+        row_argmax = torch.empty(max(total_rows, 1), dtype=torch.int32, device=dev)
+    elif row_argmax is False:
+        row_argmax = None
+    ws = _workspace(workspace, round_workspace_bytes(B, m, total_rows, V), dev)
+    _check(whiflash_round_routed(_ptr(hidden), _dtype_code(hidden), d, _ptr(W1), _ptr(b1), m,
+                                 _ptr(W2), _ptr(b2), float(tau), _ptr(delta_al), _ptr(choice),
+                                 _ptr(logits), _dtype_code(logits), B, V, stride, _ptr(row_offsets),
+                                 total_rows, K, _ptr(chain_draft), N, _ptr(parent), _ptr(draft_ids),
+                                 _ptr(d2t), d2t.numel(), _ptr(accept_len), _ptr(bonus),
+                                 _ptr(best_node), _ptr(row_argmax), _ptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(),
+                                 _stream(hidden, stream)))
+    return delta_al, choice, accept_len, bonus, best_node, row_argmax

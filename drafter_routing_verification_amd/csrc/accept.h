@@ -1,0 +1,203 @@
+// Device building blocks of the per-sequence acceptance (WhiFlash paper,
+// section 3.2): merging chunk partials into each row's greedy token, the DFlash
+// chain scan and the EAGLE-3 tree propagation.  Used by the finalize kernels.
+#pragma once
+
+#include "common.h"
+
+namespace wf {
+
+__device__ inline void better_partial(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+// t_s[i] = argmax of row (row0 + i) for i < nrows; row_argmax[row0 + i] too when given.
+// A group of G lanes (a power of two, about a quarter of the chunk count) merges
+// one row, each lane folding up to kMergePer partials whose loads are all issued
+// first; a pass over the workgroup covers 256 / G rows.
+constexpr int kMergePer = 4;
+
+__device__ inline void merge_rows(const Partial* __restrict__ part, int splits, int row0, int nrows,
+                                  int* t_s, int* __restrict__ row_argmax) {
+  int G = 1;
+  while (G * kMergePer < splits && G < 64) G <<= 1;
+  const int per_pass = kThreads / G;
+  const int sl = threadIdx.x & (G - 1);
+  for (int base = 0; base < nrows; base += per_pass) {
+    const int i = base + threadIdx.x / G;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    if (i < nrows) {
+      const Partial* p = part + static_cast<int64_t>(row0 + i) * splits;
+      for (int s0 = sl; s0 < splits; s0 += G * kMergePer) {
+        Partial q[kMergePer];
+#pragma unroll
+        for (int u = 0; u < kMergePer; ++u) {
+          const int s = s0 + u * G;
+          q[u] = s < splits ? p[s] : Partial{-INFINITY, INT_MAX};
+        }
+#pragma unroll
+        for (int u = 0; u < kMergePer; ++u) better_partial(bv, bi, q[u].val, q[u].idx);
+      }
+    }
+    for (int off = G >> 1; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      better_partial(bv, bi, ov, oi);
+    }
+    if (sl == 0 && i < nrows) {
+      if (i < kMaxSeqRows) t_s[i] = bi;
+      if (row_argmax) row_argmax[row0 + i] = bi;
+    }
+  }
+}
+
+// Chain acceptance by wave 0: n = first i < K with draft[i] != t[i], else K.
+__device__ inline void chain_accept(const int* t_s, int K, const int32_t* __restrict__ draft,
+                             int32_t* al_out, int32_t* bonus_out, int32_t* best_out) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int n = K;
+  for (int i0 = 0; i0 < K; i0 += 64) {
+    const int i = i0 + lane;
+    const bool mismatch = i < K && draft[i] != t_s[i];
+    const unsigned long long mask = __ballot(mismatch);
+    if (mask) {
+      n = i0 + __ffsll(mask) - 1;
+      break;
+    }
+  }
+  if (lane == 0) {
+    *al_out = n + 1;
+    *bonus_out = t_s[n];
+    if (best_out) *best_out = n;
+  }
+}
+
+// Tree acceptance by the whole workgroup.  anc/dep/ok are LDS scratch of kMaxSeqRows.
+__device__ inline void tree_accept(const int* t_s, int N, int V, const int32_t* __restrict__ parent,
+                            const int32_t* __restrict__ draft_ids, const int32_t* __restrict__ d2t,
+                            int Vd, int* anc, int* dep, int* ok, int* red, int32_t* al_out,
+                            int32_t* bonus_out, int32_t* best_out) {
+  const int tid = threadIdx.x;
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int u = tid + k * kThreads;
+    if (u >= N) break;
+    if (u == 0) {
+      anc[0] = 0;
+      dep[0] = 0;
+      ok[0] = 1;
+    } else {
+      const int p = parent[u];
+      const bool valid = p >= 0 && p < u;
+      const int did = draft_ids[u];
+      const int tok = (did >= 0 && did < Vd) ? d2t[did] : -1;
+      const bool match = valid && tok >= 0 && tok < V && tok == t_s[valid ? p : 0];
+      anc[u] = valid ? p : 0;
+      dep[u] = 1;
+      ok[u] = match ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  // Pointer jumping: after r rounds anc[u] is u's 2^r-th ancestor (or the root),
+  // dep[u] the number of edges to it, ok[u] the AND of the match bits on the way.
+  for (int span = 1; span < N; span <<= 1) {
+    int na[kRowsPerThread], nd[kRowsPerThread], no[kRowsPerThread];
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      const int u = tid + k * kThreads;
+      if (u < N) {
+        const int a = anc[u];
+        na[k] = anc[a];
+        nd[k] = dep[u] + dep[a];
+        no[k] = ok[u] & ok[a];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      const int u = tid + k * kThreads;
+      if (u < N) {
+        anc[u] = na[k];
+        dep[u] = nd[k];
+        ok[u] = no[k];
+      }
+    }
+    __syncthreads();
+  }
+  // Deepest accepted node, lowest index among equals: max of depth * 2^16 + (65535 - u).
+  int key = -1;
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int u = tid + k * kThreads;
+    if (u < N && ok[u]) key = max(key, (dep[u] << 16) | (0xffff - u));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) key = max(key, __shfl_xor(key, off));
+  if ((tid & 63) == 0) red[tid >> 6] = key;
+  __syncthreads();
+  if (tid == 0) {
+    int k = red[0];
+    for (int w = 1; w < kWaves; ++w) k = max(k, red[w]);
+    const int best = 0xffff - (k & 0xffff);
+    *al_out = (k >> 16) + 1;
+    *bonus_out = t_s[best];
+    if (best_out) *best_out = best;
+  }
+}
+
+// LDS used by one sequence's acceptance.
+struct AcceptLds {
+  int t_s[kMaxSeqRows], anc[kMaxSeqRows], dep[kMaxSeqRows], ok[kMaxSeqRows];
+  int red[kWaves];
+};
+
+// Arguments of the routed dispatch (see whiflash_verify_routed).
+struct RoutedArgs {
+  const Partial* part;
+  int splits, V;
+  const int32_t* row_offsets;
+  int total_rows, K;
+  const int32_t* chain_draft;
+  int N;
+  const int32_t* parent;
+  const int32_t* draft_ids;
+  const int32_t* d2t;
+  int Vd;
+  int32_t* accept_len;
+  int32_t* bonus;
+  int32_t* best_node;
+  int32_t* row_argmax;
+};
+
+// Sequence b of a routed batch verified with drafter choice c by the whole
+// workgroup: chain rows for c == 0, tree rows for c == 1, else malformed.
+__device__ inline void routed_sequence(const RoutedArgs& a, int b, int c, AcceptLds& L) {
+  const int lo = a.row_offsets[b], hi = a.row_offsets[b + 1];
+  const bool in_range = lo >= 0 && lo <= hi && hi <= a.total_rows;
+  const int rows = hi - lo;
+  const bool chain = in_range && c == 0 && rows == a.K + 1;
+  const bool tree = in_range && c == 1 && rows == a.N;
+  if (in_range) merge_rows(a.part, a.splits, lo, rows, L.t_s, a.row_argmax);
+  if (!chain && !tree) {
+    if (threadIdx.x == 0) {
+      a.accept_len[b] = 0;
+      a.bonus[b] = -1;
+      if (a.best_node) a.best_node[b] = -1;
+    }
+    return;
+  }
+  __syncthreads();
+  if (chain) {
+    chain_accept(L.t_s, a.K, a.chain_draft + static_cast<int64_t>(b) * a.K, a.accept_len + b,
+                 a.bonus + b, a.best_node ? a.best_node + b : nullptr);
+  } else {
+    const int64_t o = static_cast<int64_t>(b) * a.N;
+    tree_accept(L.t_s, a.N, a.V, a.parent + o, a.draft_ids + o, a.d2t, a.Vd, L.anc, L.dep, L.ok,
+                L.red, a.accept_len + b, a.bonus + b, a.best_node ? a.best_node + b : nullptr);
+  }
+}
+
+}  // namespace wf

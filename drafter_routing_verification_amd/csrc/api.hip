@@ -3,6 +3,7 @@
 // nothing and touches no device state.
 #include <stdint.h>
 
+#include "accept.h"
 #include "common.h"
 
 namespace {
@@ -198,6 +199,59 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
                                                   choice, K, chain_draft, N, parent, draft_ids, d2t,
                                                   Vd, accept_len, bonus, best_node, row_argmax,
                                                   stream));
+}
+
+size_t whiflash_round_workspace_bytes(int32_t B, int32_t m, int32_t total_rows, int32_t V) {
+  if (B <= 0 || m <= 0 || V <= 0) return 0;
+  return whiflash_route_workspace_bytes(B, m) + whiflash_verify_workspace_bytes(total_rows, V);
+}
+
+int32_t whiflash_round_routed(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
+                              const float* b1, int32_t m, const void* W2, const float* b2,
+                              float tau, float* delta_al, int32_t* choice, const void* logits,
+                              int32_t logits_dtype, int32_t B, int32_t V, int64_t row_stride,
+                              const int32_t* row_offsets, int32_t total_rows, int32_t K,
+                              const int32_t* chain_draft, int32_t N, const int32_t* parent,
+                              const int32_t* draft_ids, const int32_t* d2t, int32_t Vd,
+                              int32_t* accept_len, int32_t* bonus, int32_t* best_node,
+                              int32_t* row_argmax, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  // Router arguments, as whiflash_route.
+  if (!valid_dtype(hidden_dtype)) return WF_ERR_DTYPE;
+  if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
+  // Verify arguments, as whiflash_verify_routed.
+  if (total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+      N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
+    return WF_ERR_SHAPE;
+  int32_t s = check_logits(logits, logits_dtype, total_rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
+  if (!row_offsets || (K > 0 && !chain_draft) || !parent || !draft_ids || !d2t || !accept_len ||
+      !bonus)
+    return WF_ERR_NULL;
+  if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
+    return WF_ERR_SHAPE;
+  const size_t route_bytes = whiflash_route_workspace_bytes(B, m);
+  if ((s = check_workspace(workspace, workspace_bytes,
+                           whiflash_round_workspace_bytes(B, m, total_rows, V))) != WF_OK)
+    return s;
+  float* zp = static_cast<float*>(workspace);
+  wf::Partial* part = reinterpret_cast<wf::Partial*>(static_cast<char*>(workspace) + route_bytes);
+  const wf::HiddenSel direct{nullptr, nullptr, 0, 0};
+  const wf::RouterPlan plan = wf::router_plan(hidden_dtype, B, d, m, hidden, W1);
+  if (wf::launch_router_stage1(plan, hidden, direct, hidden_dtype, B, d, W1, m, zp, stream) !=
+      hipSuccess)
+    return WF_ERR_LAUNCH;
+  const wf::SweepPlan sp = wf::sweep_plan(total_rows, V);
+  if (wf::launch_sweep(logits, logits_dtype, row_stride, total_rows, V, sp, part, stream) !=
+      hipSuccess)
+    return WF_ERR_LAUNCH;
+  const wf::RoutedArgs args{part, sp.splits, V, row_offsets, total_rows, K, chain_draft, N, parent,
+                            draft_ids, d2t, Vd, accept_len, bonus, best_node, row_argmax};
+  return launch_status(wf::launch_round_finalize(hidden_dtype, plan, zp, B, m, b1, W2, b2, tau,
+                                                 delta_al, choice, args, stream));
 }
 
 int32_t whiflash_catchup_update(int32_t B, const int32_t* cur_choice, const int32_t* accept_len,

@@ -20,8 +20,8 @@ struct Partial {
   int32_t idx;
 };
 
-// How the sweep cuts rows into chunks.  `chunk` is a multiple of 8 elements so
-// every chunk starts on a 16-byte boundary for both element types.
+// How the sweep cuts rows into chunks.  `chunk` is a multiple of 256 elements,
+// so every chunk starts on a 16-byte vector boundary for both element types.
 struct SweepPlan {
   int32_t splits;  // chunks per row
   int32_t chunk;   // elements per chunk (last chunk of a row may be shorter)
@@ -108,5 +108,12 @@ hipError_t launch_entropy(const void* logits, int dtype, int64_t row_stride, int
 hipError_t launch_catchup(int32_t B, const int32_t* cur, const int32_t* accept_len,
                           const int32_t* nxt, int32_t* backlog, int32_t* switch_flag,
                           int32_t* catchup_len, hipStream_t stream);
+
+struct RoutedArgs;
+// Router finish + routed acceptance in one kernel (one workgroup per sequence).
+hipError_t launch_round_finalize(int hidden_dtype, const RouterPlan& plan, const float* zp, int32_t B,
+                                 int32_t m, const float* b1, const void* W2, const float* b2,
+                                 float tau, float* delta_al, int32_t* choice,
+                                 const RoutedArgs& args, hipStream_t stream);
 
 }  // namespace wf

@@ -1,0 +1,47 @@
+// One routed speculation round in three launches (WhiFlash paper, sections
+// 3.2 and 3.3): router stage 1 (pre-activation partials), the argmax sweep,
+// then one kernel per sequence that finishes the router (Delta-AL and the
+// drafter choice) and immediately verifies the sequence's rows with that
+// choice.  Same results as whiflash_route followed by whiflash_verify_routed;
+// one launch and one memory round trip fewer.
+#include "accept.h"
+#include "common.h"
+#include "router_math.h"
+
+namespace wf {
+namespace {
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void round_finalize_kernel(
+    const float* __restrict__ zp, int KS, int B, int m, const float* __restrict__ b1,
+    const void* __restrict__ W2, const float* __restrict__ b2, float tau,
+    float* __restrict__ delta_al, int32_t* __restrict__ choice, RoutedArgs args) {
+  __shared__ AcceptLds lds;
+  __shared__ float redf[kWaves];
+  const int b = blockIdx.x;
+  const HiddenSel direct{nullptr, nullptr, 0, 0};
+  const float dal = router_finish_sequence<DT>(zp, direct, KS, B, m, b, b1, W2, b2, redf);
+  const int c = dal > tau ? 1 : 0;
+  if (threadIdx.x == 0) {
+    delta_al[b] = dal;
+    choice[b] = c;
+  }
+  routed_sequence(args, b, c, lds);
+}
+
+}  // namespace
+
+hipError_t launch_round_finalize(int hidden_dtype, const RouterPlan& plan, const float* zp, int32_t B,
+                                 int32_t m, const float* b1, const void* W2, const float* b2,
+                                 float tau, float* delta_al, int32_t* choice,
+                                 const RoutedArgs& args, hipStream_t stream) {
+  if (hidden_dtype == WF_BF16)
+    hipLaunchKernelGGL(round_finalize_kernel<WF_BF16>, dim3(B), dim3(kThreads), 0, stream, zp,
+                       plan.slices, B, m, b1, W2, b2, tau, delta_al, choice, args);
+  else
+    hipLaunchKernelGGL(round_finalize_kernel<WF_F32>, dim3(B), dim3(kThreads), 0, stream, zp,
+                       plan.slices, B, m, b1, W2, b2, tau, delta_al, choice, args);
+  return hipGetLastError();
+}
+
+}  // namespace wf

@@ -17,6 +17,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "router_math.h"
 
 namespace wf {
 namespace {
@@ -33,16 +34,6 @@ constexpr int kChunksInFlight = 5;  // chunks whose loads are issued together
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ inline float bf16_to_f32(unsigned short b) { return __uint_as_float(static_cast<unsigned>(b) << 16); }
-
-template <int DT>
-__device__ inline float load_elem(const void* p, int64_t i) {
-  if constexpr (DT == WF_BF16) return bf16_to_f32(static_cast<const unsigned short*>(p)[i]);
-  else return static_cast<const float*>(p)[i];
-}
-
-__device__ inline float gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
 // Dot product of two 16-byte vectors, accumulated in float32.
 template <int DT>
@@ -212,55 +203,15 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
   }
 }
 
-// One workgroup per sequence: fixed-order sums over slices, units, waves.
-// Each thread owns up to kFinishPer hidden units per pass; all their partials,
-// biases and W2 entries are loaded before any is used, so a pass costs one
-// memory round trip.
-constexpr int kFinishPer = 4;
-
 template <int DT>
 __global__ __launch_bounds__(kThreads) void router_finish_kernel(
     const float* __restrict__ zp, HiddenSel sel, int KS, int B, int m, const float* __restrict__ b1,
     const void* __restrict__ W2, const float* __restrict__ b2, float tau,
     float* __restrict__ delta_al, int32_t* __restrict__ choice) {
   __shared__ float red[kWaves];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int64_t slice_stride = static_cast<int64_t>(B) * m;
-  const float* zb = zp + static_cast<int64_t>(b) * m;
-  float acc = 0.f;
-  for (int base = 0; base < m; base += kThreads * kFinishPer) {
-    float part[kMaxRouterSlices][kFinishPer];
-    float bias[kFinishPer], w2[kFinishPer];
-#pragma unroll
-    for (int u = 0; u < kFinishPer; ++u) {
-      const int j = base + u * kThreads + tid;
-      const bool ok = j < m;
-#pragma unroll
-      for (int s = 0; s < kMaxRouterSlices; ++s)
-        part[s][u] = (ok && s < KS) ? zb[s * slice_stride + j] : 0.f;
-      bias[u] = (ok && b1) ? b1[j] : 0.f;
-      w2[u] = ok ? load_elem<DT>(W2, j) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kFinishPer; ++u) {
-      if (base + u * kThreads + tid < m) {
-        float z = 0.f;
-#pragma unroll
-        for (int s = 0; s < kMaxRouterSlices; ++s)
-          if (s < KS) z += part[s][u];
-        acc += w2[u] * gelu(z + bias[u]);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if ((tid & 63) == 0) red[tid >> 6] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    float v = red[0];
-    for (int w = 1; w < kWaves; ++w) v += red[w];
-    v += b2 ? *b2 : 0.f;
-    if (hidden_row(sel, b) < 0) v = NAN;  // no hidden row for this sequence
+  const int b = blockIdx.x;
+  const float v = router_finish_sequence<DT>(zp, sel, KS, B, m, b, b1, W2, b2, red);
+  if (threadIdx.x == 0) {
     delta_al[b] = v;
     choice[b] = v > tau ? 1 : 0;
   }

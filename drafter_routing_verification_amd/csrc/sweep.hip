@@ -117,16 +117,24 @@ __global__ __launch_bounds__(kThreads) void argmax_sweep_kernel(
 }  // namespace
 
 SweepPlan sweep_plan(int32_t rows, int32_t V) {
-  // Aim for enough workgroups to keep all 256 CUs streaming with a short
-  // tail, but keep every chunk at least 2048 elements long.
-  constexpr int64_t kTargetBlocks = 8192;
+  // Chunks of ~12.7K elements (~25 KB of bf16) per workgroup: many short
+  // streams keep HBM busier than a few long ones (measured on the 4,992 x
+  // 151,936 bf16 sweep: 12 chunks per row 215.8 us, 2 chunks 219.2 us, 24
+  // chunks 244 us).  Small batches split further so a launch still has about
+  // 2048 workgroups, but never below 2048 elements per chunk.
+  constexpr int64_t kChunkTarget = 12800;
+  constexpr int64_t kMinBlocks = 2048;
   constexpr int64_t kMinChunk = 2048;
   const int64_t max_splits = V / kMinChunk > 1 ? V / kMinChunk : 1;
-  int64_t splits = (kTargetBlocks + rows - 1) / (rows > 0 ? rows : 1);
-  if (splits < 1) splits = 1;
+  int64_t splits = (V + kChunkTarget - 1) / kChunkTarget;
+  const int64_t for_blocks = (kMinBlocks + rows - 1) / (rows > 0 ? rows : 1);
+  if (splits < for_blocks) splits = for_blocks;
   if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  // Chunk starts on 256-element boundaries (512 B of bf16, 1 KiB of float32),
+  // so no memory line is shared by two chunks of a row and fetched twice.
   int64_t chunk = (V + splits - 1) / splits;
-  chunk = (chunk + 7) / 8 * 8;
+  chunk = (chunk + 255) / 256 * 256;
   splits = (V + chunk - 1) / chunk;
   return SweepPlan{static_cast<int32_t>(splits), static_cast<int32_t>(chunk)};
 }

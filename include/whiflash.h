@@ -190,6 +190,31 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
                                int32_t* row_argmax,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes whiflash_round_routed needs (router and sweep regions).
+ * Returns 0 when B, m or V is not positive. Host only. */
+size_t whiflash_round_workspace_bytes(int32_t B, int32_t m, int32_t total_rows, int32_t V);
+
+/*
+ * One routed speculation round: whiflash_route (hidden, W1, b1, W2, b2, tau ->
+ * delta_al, choice) followed by whiflash_verify_routed with that choice, with
+ * the same arguments, results and error codes as the two calls (hidden_dtype
+ * is the router's element type, logits_dtype the logits').  It runs in three
+ * launches instead of four: router stage 1, the argmax sweep, then one kernel
+ * per sequence that finishes the router and verifies the sequence.  Callers
+ * that cannot fuse the two steps (e.g. a different stream for each) use the
+ * separate entry points.
+ */
+int32_t whiflash_round_routed(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
+                              const float* b1, int32_t m, const void* W2, const float* b2,
+                              float tau, float* delta_al, int32_t* choice, const void* logits,
+                              int32_t logits_dtype, int32_t B, int32_t V, int64_t row_stride,
+                              const int32_t* row_offsets, int32_t total_rows, int32_t K,
+                              const int32_t* chain_draft, int32_t N, const int32_t* parent,
+                              const int32_t* draft_ids, const int32_t* d2t, int32_t Vd,
+                              int32_t* accept_len, int32_t* bonus, int32_t* best_node,
+                              int32_t* row_argmax, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /*
  * Lazy catch-up bookkeeping (WhiFlash paper, section 3.4 "Lazy Catch-up": the
  * inactive drafter defers its KV-cache updates; the tokens accepted while it

@@ -85,8 +85,13 @@ def test_entropy_at_accepted_rows_of_routed_workload():
     al, bo, be, _ = wf.verify_routed(logits, offs, batch.rows, choice, dev(batch.chain_draft),
                                      dev(batch.parent), dev(batch.draft_ids), dev(batch.d2t))
     torch.cuda.synchronize()
-    best = host(be)
-    rows = batch.offsets[:-1] + best
+    # the oracle's own accepted rows (the GPU path feeds its own verify output)
+    t = oracle.row_argmax(batch.logits, "bf16")
+    _, _, e_best = oracle.verify_routed(t, batch.offsets, batch.layout_choice, batch.K,
+                                        batch.chain_draft, batch.N, batch.parent, batch.draft_ids,
+                                        batch.d2t, batch.V)
+    assert np.array_equal(host(be), e_best)
+    rows = batch.offsets[:-1] + e_best
     sample = [oracle.entropy(batch.logits[r], "bf16") for r in rows[:8]]
     tau = float(np.median(sample))
     H, ch = wf.route_entropy(logits, be, tau, row0=offs)

@@ -1,0 +1,64 @@
+"""GPU parity of the fused round (whiflash_round_routed = route + verify_routed in three
+launches) against the oracle's route followed by its routed verification, and bitwise
+agreement with the two separate GPU calls."""
+
+import numpy as np
+import pytest
+import torch
+
+import drafter_routing_verification_amd as wf
+import oracle
+from gpu_helpers import check_router, dev, host, padded_logits
+from synth import make_config, make_routed_batch, make_router_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(r, rb, logits, b2):
+    args = (dev(r.hidden), dev(r.W1), dev(r.b1), dev(r.W2), b2, r.tau, logits, dev(rb.offsets),
+            rb.rows, dev(rb.chain_draft), dev(rb.parent), dev(rb.draft_ids), dev(rb.d2t))
+    out = [host(x) for x in wf.round_routed(*args)]
+    dal, ch = wf.route(dev(r.hidden), dev(r.W1), dev(r.b1), dev(r.W2), b2, r.tau)
+    sep = [host(x) for x in wf.verify_routed(logits, dev(rb.offsets), rb.rows, ch,
+                                             dev(rb.chain_draft), dev(rb.parent),
+                                             dev(rb.draft_ids), dev(rb.d2t))]
+    assert np.array_equal(out[0], host(dal)) and np.array_equal(out[1], host(ch))
+    assert all(np.array_equal(a, b) for a, b in zip(out[2:], sep))
+    return out
+
+
+def _oracle(r, rb, b2, out):
+    """The oracle's own route, then its routed verification with its own choices; sequences
+    within 1e-3 of the threshold may legitimately route differently and are not compared."""
+    e_dal, e_ch = oracle.route(r.hidden, r.W1, r.b1, r.W2, b2, r.tau, r.dtype)
+    check_router(out[0], out[1], e_dal, e_ch, r.dtype, r.tau)
+    far = np.abs(e_dal - r.tau) >= 1e-3
+    t = oracle.row_argmax(rb.logits, rb.dtype)
+    e = oracle.verify_routed(t, rb.offsets, e_ch, rb.K, rb.chain_draft, rb.N, rb.parent,
+                             rb.draft_ids, rb.d2t, rb.V)
+    assert np.array_equal(out[5], t)
+    for got, exp in zip(out[2:5], e):
+        assert np.array_equal(got[far], exp[far])
+    return far
+
+
+@pytest.mark.parametrize("B,d,m", [(12, 256, 64), (40, 2560, 1024)])
+def test_round_small(B, d, m):
+    print(f"round B={B} d={d} m={m}", flush=True)
+    r = make_router_inputs(B + 5, B, d, m, "bf16")
+    layout = np.random.default_rng(B).integers(0, 2, B).astype(np.int32)
+    rb = make_routed_batch(B + 6, layout, K=16, N=61, V=3001, Vd=500, dtype="bf16")
+    logits = padded_logits(rb.logits, 3016)
+    out = _run(r, rb, logits, 0.0)
+    _oracle(r, rb, 0.0, out)
+    # sequences whose router choice disagrees with their row count come out malformed
+    mism = out[1] != layout
+    assert np.all(out[2][mism] == 0) and np.all(out[2][~mism] >= 1)
+
+
+def test_round_routed_workload():
+    print("round on routed_bf16", flush=True)
+    batch, r = make_config(3)
+    out = _run(r, batch, dev(batch.logits), r.b2)
+    _oracle(r, batch, r.b2, out)
+    assert np.array_equal(out[1], batch.layout_choice) and out[2].min() >= 1

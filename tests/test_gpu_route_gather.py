@@ -60,6 +60,12 @@ def test_route_gather_routed_workload():
     hidden_rows = make_hidden_rows(3, batch.rows)
     dal, ch = wf.route_gather(dev(hidden_rows), be, dev(r.W1), dev(r.b1), dev(r.W2), r.b2, r.tau,
                               row0=offs)
-    sel = batch.offsets[:-1] + host(be)
+    # the oracle's own accepted rows (the GPU path feeds its own verify output)
+    t = oracle.row_argmax(batch.logits, "bf16")
+    _, _, e_best = oracle.verify_routed(t, batch.offsets, batch.layout_choice, batch.K,
+                                        batch.chain_draft, batch.N, batch.parent, batch.draft_ids,
+                                        batch.d2t, batch.V)
+    assert np.array_equal(host(be), e_best)
+    sel = batch.offsets[:-1] + e_best
     e_dal, e_ch = oracle.route_gather(hidden_rows, sel, r.W1, r.b1, r.W2, r.b2, r.tau, "bf16")
     _check(dal, ch, e_dal, e_ch, "bf16", r.tau)
