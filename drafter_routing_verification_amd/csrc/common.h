@@ -110,7 +110,7 @@ hipError_t launch_catchup(int32_t B, const int32_t* cur, const int32_t* accept_l
                           int32_t* catchup_len, hipStream_t stream);
 
 struct RoutedArgs;
-// Router finish + routed acceptance in one kernel (one workgroup per sequence).
+// Fused round: router finish + routed acceptance in one kernel per sequence.
 hipError_t launch_round_finalize(int hidden_dtype, const RouterPlan& plan, const float* zp, int32_t B,
                                  int32_t m, const float* b1, const void* W2, const float* b2,
                                  float tau, float* delta_al, int32_t* choice,

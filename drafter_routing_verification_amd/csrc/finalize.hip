@@ -22,9 +22,13 @@ __global__ __launch_bounds__(kThreads) void finalize_chain_kernel(
   __shared__ int t_s[kMaxSeqRows];
   const int b = blockIdx.x;
   const int R = K + 1;
-  merge_rows(part, splits, b * R, R, t_s, row_argmax);
+  const int32_t* dr = draft + static_cast<int64_t>(b) * K;
+  const int draft0 = K > 0 ? chain_load(dr, K) : -1;
+  MergeIn mi;
+  merge_load(mi, part, splits, b * R, R);
+  merge_finish(mi, part, splits, b * R, R, t_s, row_argmax);
   __syncthreads();
-  chain_accept(t_s, K, draft + static_cast<int64_t>(b) * K, accept_len + b, bonus + b, nullptr);
+  chain_accept(draft0, t_s, K, dr, accept_len + b, bonus + b, nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void finalize_tree_kernel(
@@ -32,20 +36,29 @@ __global__ __launch_bounds__(kThreads) void finalize_tree_kernel(
     const int32_t* __restrict__ draft_ids, const int32_t* __restrict__ d2t, int Vd,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ bonus, int32_t* __restrict__ best_node,
     int32_t* __restrict__ row_argmax) {
-  __shared__ int t_s[kMaxSeqRows], anc[kMaxSeqRows], dep[kMaxSeqRows], ok[kMaxSeqRows];
-  __shared__ int red[kWaves];
+  __shared__ AcceptLds L;
   const int b = blockIdx.x;
-  merge_rows(part, splits, b * N, N, t_s, row_argmax);
-  __syncthreads();
   const int64_t o = static_cast<int64_t>(b) * N;
-  tree_accept(t_s, N, V, parent + o, draft_ids + o, d2t, Vd, anc, dep, ok, red, accept_len + b,
-              bonus + b, best_node ? best_node + b : nullptr);
+  TreeIn ti;
+  tree_load_ids(ti, N, parent + o, draft_ids + o);
+  MergeIn mi;
+  merge_load(mi, part, splits, b * N, N);
+  tree_load_tokens(ti, d2t, Vd, V);
+  merge_finish(mi, part, splits, b * N, N, L.t_s, row_argmax);
+  __syncthreads();
+  tree_accept(ti, L.t_s, N, L.anc, L.dep, L.ok, L.red, accept_len + b, bonus + b,
+              best_node ? best_node + b : nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void finalize_routed_kernel(RoutedArgs args,
                                                                    const int32_t* __restrict__ choice) {
   __shared__ AcceptLds lds;
-  routed_sequence(args, blockIdx.x, choice[blockIdx.x], lds);
+  const int b = blockIdx.x;
+  RoutedIn in;
+  routed_load_phase1(in, args, b);
+  const int c = choice[b];
+  routed_load_phase2(in, args);
+  routed_accept(in, args, b, c, lds);
 }
 
 }  // namespace

@@ -1,9 +1,11 @@
-// One routed speculation round in three launches (WhiFlash paper, sections
-// 3.2 and 3.3): router stage 1 (pre-activation partials), the argmax sweep,
-// then one kernel per sequence that finishes the router (Delta-AL and the
-// drafter choice) and immediately verifies the sequence's rows with that
-// choice.  Same results as whiflash_route followed by whiflash_verify_routed;
-// one launch and one memory round trip fewer.
+// One routed speculation round (WhiFlash paper, sections 3.2 and 3.3): the
+// neural router, then greedy verification of each sequence with the drafter
+// the router chose.  Same results as whiflash_route followed by
+// whiflash_verify_routed, in three launches instead of four: router stage 1,
+// the argmax sweep, then one kernel per sequence that finishes the router
+// (Delta-AL and the drafter choice) and verifies the sequence with it.
+// (Running the router's workgroups inside the sweep's launch was measured
+// slower: latency-bound router tiles stretched the 217 us sweep to 245 us.)
 #include "accept.h"
 #include "common.h"
 #include "router_math.h"
@@ -20,13 +22,20 @@ __global__ __launch_bounds__(kThreads) void round_finalize_kernel(
   __shared__ float redf[kWaves];
   const int b = blockIdx.x;
   const HiddenSel direct{nullptr, nullptr, 0, 0};
-  const float dal = router_finish_sequence<DT>(zp, direct, KS, B, m, b, b1, W2, b2, redf);
+  // Phase 1: every load that depends on nothing else (router partials, offsets,
+  // drafts, parents, draft ids); phase 2: chunk partials and d2t entries.
+  RoutedIn in;
+  routed_load_phase1(in, args, b);
+  FinishIn fin;
+  finish_load_pass<DT>(fin, zp, KS, B, m, b, 0, b1, W2);
+  routed_load_phase2(in, args);
+  const float dal = router_finish_compute<DT>(fin, zp, direct, KS, B, m, b, b1, W2, b2, redf);
   const int c = dal > tau ? 1 : 0;
   if (threadIdx.x == 0) {
     delta_al[b] = dal;
     choice[b] = c;
   }
-  routed_sequence(args, b, c, lds);
+  routed_accept(in, args, b, c, lds);
 }
 
 }  // namespace

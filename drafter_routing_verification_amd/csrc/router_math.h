@@ -20,47 +20,66 @@ __device__ inline float load_elem(const void* p, int64_t i) {
 
 __device__ inline float gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
-// Each thread owns up to kFinishPer hidden units per pass; all their partials,
-// biases and W2 entries are loaded before any is used, so a pass costs one
-// memory round trip.
+// Each thread owns up to kFinishPer hidden units per pass of the finish; all
+// their partials, biases and W2 entries are loaded before any is used, so a
+// pass costs one memory round trip.
 constexpr int kFinishPer = 4;
 
-// Delta-AL of sequence b from zp[s][b][j] (s < KS), computed by the whole
-// workgroup; `red` is LDS of kWaves floats.  Every thread returns the value;
-// NaN when the sequence has no hidden row.
+// Loads of the first pass of the finish of sequence b (hidden units
+// j = threadIdx.x + u * 256, u < kFinishPer), issued before any is used.
+struct FinishIn {
+  float part[kMaxRouterSlices][kFinishPer];
+  float bias[kFinishPer], w2[kFinishPer];
+};
+
 template <int DT>
-__device__ inline float router_finish_sequence(const float* __restrict__ zp, const HiddenSel& sel,
-                                               int KS, int B, int m, int b,
-                                               const float* __restrict__ b1,
-                                               const void* __restrict__ W2,
-                                               const float* __restrict__ b2, float* red) {
-  const int tid = threadIdx.x;
+__device__ inline void finish_load_pass(FinishIn& in, const float* __restrict__ zp, int KS, int B,
+                                        int m, int b, int base, const float* __restrict__ b1,
+                                        const void* __restrict__ W2) {
   const int64_t slice_stride = static_cast<int64_t>(B) * m;
   const float* zb = zp + static_cast<int64_t>(b) * m;
-  float acc = 0.f;
-  for (int base = 0; base < m; base += kThreads * kFinishPer) {
-    float part[kMaxRouterSlices][kFinishPer];
-    float bias[kFinishPer], w2[kFinishPer];
 #pragma unroll
-    for (int u = 0; u < kFinishPer; ++u) {
-      const int j = base + u * kThreads + tid;
-      const bool ok = j < m;
+  for (int u = 0; u < kFinishPer; ++u) {
+    const int j = base + u * kThreads + threadIdx.x;
+    const bool ok = j < m;
+#pragma unroll
+    for (int s = 0; s < kMaxRouterSlices; ++s)
+      in.part[s][u] = (ok && s < KS) ? zb[s * slice_stride + j] : 0.f;
+    in.bias[u] = (ok && b1) ? b1[j] : 0.f;
+    in.w2[u] = ok ? load_elem<DT>(W2, j) : 0.f;
+  }
+}
+
+__device__ inline float finish_fold_pass(const FinishIn& in, int KS, int m, int base, float acc) {
+#pragma unroll
+  for (int u = 0; u < kFinishPer; ++u) {
+    if (base + u * kThreads + static_cast<int>(threadIdx.x) < m) {
+      float z = 0.f;
 #pragma unroll
       for (int s = 0; s < kMaxRouterSlices; ++s)
-        part[s][u] = (ok && s < KS) ? zb[s * slice_stride + j] : 0.f;
-      bias[u] = (ok && b1) ? b1[j] : 0.f;
-      w2[u] = ok ? load_elem<DT>(W2, j) : 0.f;
+        if (s < KS) z += in.part[s][u];
+      acc += in.w2[u] * gelu(z + in.bias[u]);
     }
-#pragma unroll
-    for (int u = 0; u < kFinishPer; ++u) {
-      if (base + u * kThreads + tid < m) {
-        float z = 0.f;
-#pragma unroll
-        for (int s = 0; s < kMaxRouterSlices; ++s)
-          if (s < KS) z += part[s][u];
-        acc += w2[u] * gelu(z + bias[u]);
-      }
-    }
+  }
+  return acc;
+}
+
+// Delta-AL of sequence b from zp[s][b][j] (s < KS), computed by the whole
+// workgroup, given the first pass already loaded in `first`; `red` is LDS of
+// kWaves floats.  Every thread returns the value; NaN when the sequence has
+// no hidden row.
+template <int DT>
+__device__ inline float router_finish_compute(const FinishIn& first, const float* __restrict__ zp,
+                                              const HiddenSel& sel, int KS, int B, int m, int b,
+                                              const float* __restrict__ b1,
+                                              const void* __restrict__ W2,
+                                              const float* __restrict__ b2, float* red) {
+  const int tid = threadIdx.x;
+  float acc = finish_fold_pass(first, KS, m, 0, 0.f);
+  for (int base = kThreads * kFinishPer; base < m; base += kThreads * kFinishPer) {
+    FinishIn in;
+    finish_load_pass<DT>(in, zp, KS, B, m, b, base, b1, W2);
+    acc = finish_fold_pass(in, KS, m, base, acc);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -72,6 +91,17 @@ __device__ inline float router_finish_sequence(const float* __restrict__ zp, con
   v += b2 ? *b2 : 0.f;
   if (hidden_row(sel, b) < 0) v = NAN;  // no hidden row for this sequence
   return v;
+}
+
+template <int DT>
+__device__ inline float router_finish_sequence(const float* __restrict__ zp, const HiddenSel& sel,
+                                               int KS, int B, int m, int b,
+                                               const float* __restrict__ b1,
+                                               const void* __restrict__ W2,
+                                               const float* __restrict__ b2, float* red) {
+  FinishIn first;
+  finish_load_pass<DT>(first, zp, KS, B, m, b, 0, b1, W2);
+  return router_finish_compute<DT>(first, zp, sel, KS, B, m, b, b1, W2, b2, red);
 }
 
 }  // namespace wf

@@ -1,117 +1,16 @@
-// Full-vocabulary argmax sweep over target logits rows (greedy verification:
-// the target's token at each drafted position is the lowest index holding the
-// row maximum; WhiFlash paper, section 3.2, with greedy decoding).
-//
-// HBM-bound streaming kernel.  Each workgroup owns one chunk of one row and
-// reads it once with 16-byte loads, 256 threads side by side so every wave64
-// load instruction covers 1 KiB of contiguous memory.  A thread keeps its
-// running maximum and the 16-byte vector where it first reached it (strict
-// ">" in increasing index order keeps the earliest) together with that
-// vector's data, and recovers the element index from it at the end.  The per-chunk
-// (max, index) pair is reduced across the wave with cross-lane shuffles and
-// across the four waves in LDS; ties go to the lower index at every level.
-#include <math.h>
-
+// Full-vocabulary argmax sweep kernel: one workgroup per chunk of a row
+// (the per-chunk work is in sweep_body.h).
 #include "common.h"
-#include "elem.h"
+#include "sweep_body.h"
 
 namespace wf {
 namespace {
-
-constexpr int kUnroll = 8;  // 16-byte loads in flight per thread
-
-// (v, i) beats (bv, bi) when larger, or equal with a lower index.
-__device__ inline void take_better(float& bv, int& bi, float v, int i) {
-  if (v > bv || (v == bv && i < bi)) {
-    bv = v;
-    bi = i;
-  }
-}
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void argmax_sweep_kernel(
     const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
     int chunk_vecs, int nvec, Partial* __restrict__ part) {
-  using E = Elem<DT>;
-  const int blk = blockIdx.x;
-  const int row = blk / splits;
-  const int c = blk - row * splits;
-  const unsigned char* rowp = logits + static_cast<int64_t>(row) * row_bytes;
-  const u32x4* vp = reinterpret_cast<const u32x4*>(rowp);
-  const int tid = threadIdx.x;
-  const int v0 = c * chunk_vecs;
-  const int v1 = min(v0 + chunk_vecs, nvec);
-
-  // The vector where `best` was first reached stays in registers, so the index
-  // is recovered without a dependent re-load after the stream.
-  float best = -INFINITY;
-  int bestv = -1;
-  u32x4 bestd = {0u, 0u, 0u, 0u};
-  int v = v0 + tid;
-  for (; v + (kUnroll - 1) * kThreads < v1; v += kUnroll * kThreads) {
-    u32x4 d[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) d[u] = load16(vp + v + u * kThreads);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float m = E::vmax(d[u]);
-      if (m > best) {
-        best = m;
-        bestv = v + u * kThreads;
-        bestd = d[u];
-      }
-    }
-  }
-  for (; v < v1; v += kThreads) {
-    const u32x4 d = load16(vp + v);
-    const float m = E::vmax(d);
-    if (m > best) {
-      best = m;
-      bestv = v;
-      bestd = d;
-    }
-  }
-
-  int idx = INT_MAX;
-  if (v0 + tid < v1) {
-    // No element above -inf (all -inf, or NaN): the thread's first element is
-    // the first occurrence of -inf, and a valid index in every case.
-    idx = bestv >= 0 ? bestv * E::kPerVec + E::first_equal(bestd, best) : (v0 + tid) * E::kPerVec;
-  } else {
-    best = -INFINITY;
-  }
-  // Elements past the last full vector (V not a multiple of the vector width).
-  if (c == splits - 1 && tid == 0) {
-    for (int e = nvec * E::kPerVec; e < V; ++e) {
-      const float x = E::scalar(rowp, e);
-      if (x > best || idx == INT_MAX) {
-        best = x;
-        idx = e;
-      }
-    }
-  }
-
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(best, off);
-    const int oi = __shfl_xor(idx, off);
-    take_better(best, idx, ov, oi);
-  }
-  __shared__ float sv[kWaves];
-  __shared__ int si[kWaves];
-  const int lane = tid & 63, wave = tid >> 6;
-  if (lane == 0) {
-    sv[wave] = best;
-    si[wave] = idx;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float bv = sv[0];
-    int bi = si[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) take_better(bv, bi, sv[w], si[w]);
-    part[blk] = Partial{bv, bi};
-  }
+  sweep_chunk<DT>(blockIdx.x, logits, row_bytes, V, splits, chunk_vecs, nvec, part);
 }
 
 }  // namespace

@@ -1,6 +1,6 @@
 """GPU parity of the fused round (whiflash_round_routed = route + verify_routed in three
-launches) against the oracle's route followed by its routed verification, and bitwise
-agreement with the two separate GPU calls."""
+launches) against the oracle's route followed by its routed verification, and
+agreement with the two separate GPU calls (the router may be summed in another order)."""
 
 import numpy as np
 import pytest
@@ -22,8 +22,14 @@ def _run(r, rb, logits, b2):
     sep = [host(x) for x in wf.verify_routed(logits, dev(rb.offsets), rb.rows, ch,
                                              dev(rb.chain_draft), dev(rb.parent),
                                              dev(rb.draft_ids), dev(rb.d2t))]
-    assert np.array_equal(out[0], host(dal)) and np.array_equal(out[1], host(ch))
-    assert all(np.array_equal(a, b) for a, b in zip(out[2:], sep))
+    # The fused round may sum the router in another order than whiflash_route:
+    # the two float32 results agree closely, and so does everything downstream.
+    dal_s, ch_s = host(dal), host(ch)
+    assert np.all(np.abs(out[0] - dal_s) <= 1e-4 * np.maximum(1.0, np.abs(dal_s)))
+    same = out[1] == ch_s
+    assert np.all(same | (np.abs(dal_s - r.tau) < 1e-3))
+    assert all(np.array_equal(a[same], b[same]) for a, b in zip(out[2:5], sep[:3]))
+    assert np.array_equal(out[5], sep[3])
     return out
 
 
@@ -42,7 +48,7 @@ def _oracle(r, rb, b2, out):
     return far
 
 
-@pytest.mark.parametrize("B,d,m", [(12, 256, 64), (40, 2560, 1024)])
+@pytest.mark.parametrize("B,d,m", [(12, 256, 64), (40, 2560, 1024), (16, 104, 70), (70, 512, 50)])
 def test_round_small(B, d, m):
     print(f"round B={B} d={d} m={m}", flush=True)
     r = make_router_inputs(B + 5, B, d, m, "bf16")
