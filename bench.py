@@ -34,7 +34,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "argmax_sweep_traffic.json")
-SWEEP_SRC = os.path.join(ROOT, "drafter_routing_verification_amd", "csrc", "sweep.hip")
+# Sources of the argmax sweep kernel: a change to any of them voids the stored counters.
+SWEEP_SRCS = [os.path.join(ROOT, "drafter_routing_verification_amd", "csrc", f)
+              for f in ("sweep.hip", "sweep_body.h", "elem.h")]
 
 
 def _parse():
@@ -44,9 +46,10 @@ def _parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", choices=["routed", "sweep"], default="routed")
     p.add_argument("--pool", type=int, default=4, help="distinct rounds resident in HBM (sweep)")
-    p.add_argument("--mode", choices=["fused", "separate"], default="fused",
+    p.add_argument("--mode", choices=["fused", "separate", "early-exit"], default="fused",
                    help="routed workload: whiflash_round_routed, or whiflash_route then "
-                        "whiflash_verify_routed")
+                        "whiflash_verify_routed; sweep workload: early-exit verifies with "
+                        "whiflash_verify_chain_early_exit (reads rows 0..n only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -60,8 +63,11 @@ def _to_dev(a, torch, dev):
 
 
 def _sweep_source_hash() -> str:
-    with open(SWEEP_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in SWEEP_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(workload: str, launches_bytes: float):
@@ -200,10 +206,23 @@ class Sweep:
         self.rws = torch.empty(wf.route_workspace_bytes(self.B, self.m), dtype=torch.uint8, device=dev)
         self.vws = torch.empty(wf.verify_workspace_bytes(self.rows, self.V), dtype=torch.uint8,
                                device=dev)
+        self.ews = torch.empty(wf.early_exit_workspace_bytes(self.B, self.K, self.V),
+                               dtype=torch.uint8, device=dev)
+        self.early = False
         self.wf = wf
         self.setup_s = time.time() - t0
         self.logits_bytes = self.rows * self.V * 2
         self.step_bytes = self.logits_bytes + self.router_bytes + (self.B * self.K + 4 * self.B) * 4
+
+    def use_early_exit(self):
+        """Verify with the early-exit schedule; the bytes it needs per round are those of
+        rows 0..n of every sequence (sum of accept lengths), averaged over the pool."""
+        self.early = True
+        need = []
+        for i in range(len(self.pool)):
+            self.verify(i)
+            need.append(int(self.al.sum().item()) * self.V * 2)
+        self.needed_bytes = sum(need) / len(need)
 
     def route(self, i):
         p = self.pool[i % len(self.pool)]
@@ -212,8 +231,13 @@ class Sweep:
 
     def verify(self, i):
         p = self.pool[i % len(self.pool)]
-        self.wf.verify_chain(p["logits"], p["draft"], row_argmax=False, accept_len=self.al,
-                             bonus=self.bonus, workspace=self.vws)
+        if self.early:
+            self.wf.verify_chain_early_exit(p["logits"], p["draft"], row_argmax=False,
+                                            accept_len=self.al, bonus=self.bonus,
+                                            workspace=self.ews)
+        else:
+            self.wf.verify_chain(p["logits"], p["draft"], row_argmax=False, accept_len=self.al,
+                                 bonus=self.bonus, workspace=self.vws)
 
     def check(self):
         al = self.al.cpu().numpy()
@@ -264,6 +288,12 @@ def main():
           file=sys.stderr, flush=True)
 
     fused = args.mode == "fused" and hasattr(work, "fused_step")
+    early = args.mode == "early-exit"
+    if early:
+        if not hasattr(work, "use_early_exit"):
+            print("--mode early-exit applies to the chain-only sweep workload", file=sys.stderr)
+            sys.exit(2)
+        work.use_early_exit()
 
     def step(i):
         if fused:
@@ -307,8 +337,14 @@ def main():
 
     ms_per_step = gpu_total_ms / K
     rounds_per_s = 1000.0 / ms_per_step
-    achieved = work.logits_bytes / verify_s / 1e9
-    traffic = _traffic(work.name, work.logits_bytes)
+    # Algorithmic bytes of the verify call: every logits row, or with the early-exit
+    # schedule only rows 0..n of each sequence (what it must read at the least).
+    alg_bytes = work.needed_bytes if early else work.logits_bytes
+    achieved = alg_bytes / verify_s / 1e9
+    traffic = None if early else _traffic(work.name, work.logits_bytes)
+    mode = ("whiflash_round_routed" if fused else
+            "whiflash_route + whiflash_verify_chain_early_exit" if early else
+            "whiflash_route + whiflash_verify_*")
     out = {
         "metric": "verify+route rounds/s (1 GPU); logits HBM GB/s of the verify sweep",
         "value": round(rounds_per_s, 2),
@@ -322,8 +358,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; planted-argmax logits, random trees, random router weights)",
-        "config": {"workload": work.name, "mode": "whiflash_round_routed" if fused else
-                   "whiflash_route + whiflash_verify_*", "batch": work.B, "logits_rows": work.rows,
+        "config": {"workload": work.name, "mode": mode, "batch": work.B, "logits_rows": work.rows,
                    "vocab": work.V, "hidden": 2560, "router_width": 1024,
                    "logits_bytes_per_round": work.logits_bytes,
                    "bytes_per_round": work.step_bytes},
@@ -332,8 +367,11 @@ def main():
         "verify_us": round(verify_s * 1e6, 2),
         "wall_ms_per_step": round(wall * 1000 / K, 5),
         "mean_accept_len": round(mean_al, 3),
+        **({"logits_bytes_needed_per_round": round(alg_bytes)} if early else {}),
         "roofline": {
-            "kernel": "whiflash_verify_* call: argmax sweep + acceptance kernel, back to back",
+            "kernel": ("whiflash_verify_chain_early_exit call: flag clear + early-exit sweep + "
+                       "acceptance, back to back; bytes = rows 0..n" if early else
+                       "whiflash_verify_* call: argmax sweep + acceptance kernel, back to back"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     route_gather(hidden_rows, pos, W1, b1, W2, b2, tau, row0=None, rows_per_seq=0)
                                                           -> (delta_al, choice)
     verify_chain(logits, draft)                           -> (accept_len, bonus, row_argmax)
+    verify_chain_early_exit(logits, draft)                -> (accept_len, bonus, row_argmax)
     verify_tree(logits, parent, draft_ids, d2t)           -> (accept_len, bonus, best_node, row_argmax)
     verify_routed(logits, row_offsets, total_rows, choice, chain_draft, parent, draft_ids, d2t)
                                                           -> (accept_len, bonus, best_node, row_argmax)
@@ -35,6 +36,9 @@ from ._binding import (  # noqa: F401
     whiflash_route_gather,
     verify_chain,
     verify_tree,
+    verify_chain_early_exit,
+    early_exit_workspace_bytes,
+    whiflash_verify_chain_early_exit,
     verify_routed,
     route_entropy,
     entropy_workspace_bytes,

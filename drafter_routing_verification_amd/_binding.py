@@ -29,6 +29,9 @@ _SIGNATURES = {
                                 _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_verify_chain": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
                                        _c_p, _c_p, _c_sz, _c_p]),
+    "whiflash_early_exit_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32]),
+    "whiflash_verify_chain_early_exit": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p,
+                                                  _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_verify_tree": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
                                       _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_route_gather": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p,
@@ -92,6 +95,14 @@ def whiflash_route(*args):
 
 def whiflash_verify_chain(*args):
     return lib().whiflash_verify_chain(*args)
+
+
+def whiflash_verify_chain_early_exit(*args):
+    return lib().whiflash_verify_chain_early_exit(*args)
+
+
+def early_exit_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(lib().whiflash_early_exit_workspace_bytes(B, K, V))
 
 
 def whiflash_verify_tree(*args):
@@ -283,6 +294,31 @@ def verify_chain(logits, draft, *, row_argmax=True, accept_len=None, bonus=None,
                                  _ptr(accept_len), _ptr(bonus), _ptr(row_argmax), _ptr(ws),
                                  0 if ws is None else ws.numel() * ws.element_size(),
                                  _stream(logits, stream)))
+    return accept_len, bonus, row_argmax
+
+
+def verify_chain_early_exit(logits, draft, *, row_argmax=True, accept_len=None, bonus=None,
+                            workspace=None, stream=None):
+    """DFlash block verification that reads only rows 0..n of each sequence (n = first
+    mismatch).  Arguments as verify_chain; row_argmax holds -1 after each sequence's n."""
+    _device_tensor(draft, "draft")
+    B, K = draft.shape
+    rows = B * (K + 1)
+    V, stride = _rows_view(logits, rows)
+    _i32(draft, "draft")
+    dev = logits.device
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    bonus = torch.empty(B, dtype=torch.int32, device=dev) if bonus is None else bonus
+    if row_argmax is True:
+        row_argmax = torch.empty(rows, dtype=torch.int32, device=dev)
+    elif row_argmax is False:
+        row_argmax = None
+    ws = _workspace(workspace, early_exit_workspace_bytes(B, K, V), dev)
+    _check(whiflash_verify_chain_early_exit(_ptr(logits), _dtype_code(logits), B, K, V, stride,
+                                            _ptr(draft), _ptr(accept_len), _ptr(bonus),
+                                            _ptr(row_argmax), _ptr(ws),
+                                            0 if ws is None else ws.numel() * ws.element_size(),
+                                            _stream(logits, stream)))
     return accept_len, bonus, row_argmax
 
 

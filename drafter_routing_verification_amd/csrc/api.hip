@@ -32,8 +32,8 @@ int32_t check_logits(const void* logits, int32_t dtype, int32_t rows, int32_t V,
   if (rows > 0 && logits == nullptr) return WF_ERR_NULL;
   if (!aligned16(logits) || (row_stride * elem_bytes(dtype)) % 16 != 0) return WF_ERR_ALIGN;
   const wf::SweepPlan plan = wf::sweep_plan(rows, V);
-  // 1-D grid of 256-thread workgroups: keep the work-item count below 2^32.
-  if (static_cast<int64_t>(rows) * plan.splits * wf::kThreads >= (int64_t{1} << 32))
+  // 1-D grid of workgroups of up to 1024 threads: keep the work-item count below 2^32.
+  if (static_cast<int64_t>(rows) * plan.splits * 1024 >= (int64_t{1} << 32))
     return WF_ERR_SHAPE;
   return WF_OK;
 }
@@ -147,6 +147,40 @@ int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int3
     return WF_ERR_LAUNCH;
   return launch_status(wf::launch_finalize_chain(part, plan.splits, B, K, draft, accept_len, bonus,
                                                  row_argmax, stream));
+}
+
+size_t whiflash_early_exit_workspace_bytes(int32_t B, int32_t K, int32_t V) {
+  if (B <= 0 || K < 0 || V <= 0) return 0;
+  const wf::SweepPlan plan = wf::early_exit_plan(B, V);
+  // Per-sequence mismatch flags, then the chunk partials of every row.
+  return round_up(static_cast<size_t>(B) * sizeof(int32_t), kWorkspaceAlign) +
+         round_up(static_cast<size_t>(B) * (K + 1) * plan.splits * sizeof(wf::Partial),
+                  kWorkspaceAlign);
+}
+
+int32_t whiflash_verify_chain_early_exit(const void* logits, int32_t dtype, int32_t B, int32_t K,
+                                         int32_t V, int64_t row_stride, const int32_t* draft,
+                                         int32_t* accept_len, int32_t* bonus, int32_t* row_argmax,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  if (B < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
+  const int64_t rows64 = static_cast<int64_t>(B) * (K + 1);
+  if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
+  const int32_t rows = static_cast<int32_t>(rows64);
+  int32_t s = check_logits(logits, dtype, rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!accept_len || !bonus || (K > 0 && !draft)) return WF_ERR_NULL;
+  const wf::SweepPlan plan = wf::early_exit_plan(B, V);
+  if (rows64 * plan.splits * 1024 >= (int64_t{1} << 32)) return WF_ERR_SHAPE;
+  const size_t need = whiflash_early_exit_workspace_bytes(B, K, V);
+  if ((s = check_workspace(workspace, workspace_bytes, need)) != WF_OK) return s;
+  int* flags = static_cast<int*>(workspace);
+  wf::Partial* part = reinterpret_cast<wf::Partial*>(
+      static_cast<char*>(workspace) + round_up(static_cast<size_t>(B) * sizeof(int32_t), kWorkspaceAlign));
+  return launch_status(wf::launch_early_exit_chain(logits, dtype, row_stride, B, K, V, plan, draft,
+                                                   flags, part, accept_len, bonus, row_argmax,
+                                                   stream));
 }
 
 int32_t whiflash_verify_tree(const void* logits, int32_t dtype, int32_t B, int32_t N, int32_t V,

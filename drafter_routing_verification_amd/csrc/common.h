@@ -55,6 +55,14 @@ __device__ inline int64_t hidden_row(const HiddenSel& s, int b) {
 hipError_t launch_sweep(const void* logits, int dtype, int64_t row_stride, int32_t rows, int32_t V,
                         SweepPlan plan, Partial* part, hipStream_t stream);
 
+// Early-exit chain verification: chunk plan, and clear + sweep + accept launches.
+// flags holds B int32 (cleared by the call), part B * (K + 1) * plan.splits partials.
+SweepPlan early_exit_plan(int32_t B, int32_t V);
+hipError_t launch_early_exit_chain(const void* logits, int dtype, int64_t row_stride, int32_t B,
+                                   int32_t K, int32_t V, SweepPlan plan, const int32_t* draft,
+                                   int* flags, Partial* part, int32_t* accept_len, int32_t* bonus,
+                                   int32_t* row_argmax, hipStream_t stream);
+
 hipError_t launch_finalize_chain(const Partial* part, int32_t splits, int32_t B, int32_t K,
                                  const int32_t* draft, int32_t* accept_len, int32_t* bonus,
                                  int32_t* row_argmax, hipStream_t stream);

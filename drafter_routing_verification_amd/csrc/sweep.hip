@@ -3,26 +3,39 @@
 #include "common.h"
 #include "sweep_body.h"
 
+#ifndef WF_SWEEP_THREADS
+#define WF_SWEEP_THREADS 256
+#endif
+#ifndef WF_SWEEP_CHUNK
+#define WF_SWEEP_CHUNK 12800
+#endif
+
 namespace wf {
 namespace {
 
+constexpr int kSweepThreads = WF_SWEEP_THREADS;
+
 template <int DT>
-__global__ __launch_bounds__(kThreads) void argmax_sweep_kernel(
+__global__ __launch_bounds__(kSweepThreads) void argmax_sweep_kernel(
     const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
     int chunk_vecs, int nvec, Partial* __restrict__ part) {
-  sweep_chunk<DT>(blockIdx.x, logits, row_bytes, V, splits, chunk_vecs, nvec, part);
+  sweep_chunk<DT, kSweepThreads>(blockIdx.x, logits, row_bytes, V, splits, chunk_vecs, nvec, part);
 }
 
 }  // namespace
 
 SweepPlan sweep_plan(int32_t rows, int32_t V) {
-  // Chunks of ~12.7K elements (~25 KB of bf16) per workgroup: many short
-  // streams keep HBM busier than a few long ones (measured on the 4,992 x
-  // 151,936 bf16 sweep: 12 chunks per row 215.8 us, 2 chunks 219.2 us, 24
-  // chunks 244 us).  Small batches split further so a launch still has about
-  // 2048 workgroups, but never below 2048 elements per chunk.
-  constexpr int64_t kChunkTarget = 12800;
-  constexpr int64_t kMinBlocks = 2048;
+  // 256-thread workgroups over chunks of ~12.8K elements (~25 KB of bf16),
+  // 12 per 151,936-wide row.  Same-process A/B on the 4,992-row routed and
+  // 4,352-row chain workloads (median of 5 interleaved trials): this 219.0 /
+  // 191.8 us; 512 threads over 30,720-element chunks 246.8 / 215.9 us, or
+  // 223.4 / 197.3 us with every load batch issued whole; 256 threads with
+  // whole batches 228.6 / 197.6 us.  Earlier: 2 chunks per row 219.2 us and 24
+  // chunks 244 us against 215.8 us for 12.  Small batches split further so a
+  // launch still has about 2048 workgroups, but never below 2048 elements per
+  // chunk.
+  constexpr int64_t kChunkTarget = WF_SWEEP_CHUNK;
+  constexpr int64_t kMinBlocks = 2048 * 256 / kSweepThreads;
   constexpr int64_t kMinChunk = 2048;
   const int64_t max_splits = V / kMinChunk > 1 ? V / kMinChunk : 1;
   int64_t splits = (V + kChunkTarget - 1) / kChunkTarget;
@@ -46,12 +59,12 @@ hipError_t launch_sweep(const void* logits, int dtype, int64_t row_stride, int32
   if (dtype == WF_BF16) {
     using E = Elem<WF_BF16>;
     hipLaunchKernelGGL(argmax_sweep_kernel<WF_BF16>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, stream, base, row_stride * E::kBytes, V, plan.splits,
+                       dim3(kSweepThreads), 0, stream, base, row_stride * E::kBytes, V, plan.splits,
                        plan.chunk / E::kPerVec, V / E::kPerVec, part);
   } else {
     using E = Elem<WF_F32>;
     hipLaunchKernelGGL(argmax_sweep_kernel<WF_F32>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, stream, base, row_stride * E::kBytes, V, plan.splits,
+                       dim3(kSweepThreads), 0, stream, base, row_stride * E::kBytes, V, plan.splits,
                        plan.chunk / E::kPerVec, V / E::kPerVec, part);
   }
   return hipGetLastError();

@@ -1,15 +1,15 @@
 // The argmax sweep over one chunk of one logits row (greedy verification:
 // the target's token at each drafted position is the lowest index holding the
 // row maximum; WhiFlash paper, section 3.2, with greedy decoding), run by one
-// 256-thread workgroup.  Shared by the sweep kernel and the fused round kernel.
+// workgroup.  Shared by the sweep kernel and the fused round kernel.
 //
-// HBM-bound streaming.  The 256 threads read the chunk side by side with
+// HBM-bound streaming.  The threads read the chunk side by side with
 // 16-byte non-temporal loads, so every wave64 load instruction covers 1 KiB of
 // contiguous memory.  A thread keeps its running maximum, the 16-byte vector
 // where it first reached it (strict ">" in increasing index order keeps the
 // earliest) and that vector's data, and recovers the element index from it at
 // the end.  The chunk's (max, index) pair is reduced across the wave with
-// cross-lane shuffles and across the four waves in LDS; ties go to the lower
+// cross-lane shuffles and across the waves in LDS; ties go to the lower
 // index at every level.
 #pragma once
 
@@ -30,11 +30,20 @@ __device__ inline void take_better(float& bv, int& bi, float v, int i) {
   }
 }
 
-template <int DT>
-__device__ inline void sweep_chunk(int blk, const unsigned char* __restrict__ logits,
-                                   int64_t row_bytes, int V, int splits, int chunk_vecs, int nvec,
-                                   Partial* __restrict__ part) {
+// Returns the chunk's (max, index) in thread 0 (other threads: unspecified).
+// NT threads per workgroup (a multiple of 64).  Two forms of the stream:
+//   kBatchTail false: full batches of kUnroll loads, then the remainder one
+//     load at a time.  Best when every resident workgroup streams (the full
+//     sweep: 32 waves per CU each with a load in flight keep HBM busy).
+//   kBatchTail true: every batch, the last partial one included, issues all
+//     its loads before the first compare (missing loads masked off).  Best
+//     when fewer workgroups stream at once (the early-exit schedule).
+template <int DT, int NT = kThreads, bool kBatchTail = false>
+__device__ inline Partial sweep_chunk(int blk, const unsigned char* __restrict__ logits,
+                                      int64_t row_bytes, int V, int splits, int chunk_vecs, int nvec,
+                                      Partial* __restrict__ part) {
   using E = Elem<DT>;
+  constexpr int kW = NT / 64;
   const int row = blk / splits;
   const int c = blk - row * splits;
   const unsigned char* rowp = logits + static_cast<int64_t>(row) * row_bytes;
@@ -48,28 +57,48 @@ __device__ inline void sweep_chunk(int blk, const unsigned char* __restrict__ lo
   float best = -INFINITY;
   int bestv = -1;
   u32x4 bestd = {0u, 0u, 0u, 0u};
-  int v = v0 + tid;
-  for (; v + (kUnroll - 1) * kThreads < v1; v += kUnroll * kThreads) {
-    u32x4 d[kUnroll];
+  if constexpr (kBatchTail) {
+    for (int v = v0 + tid; v < v1; v += kUnroll * NT) {
+      u32x4 d[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) d[u] = load16(vp + v + u * kThreads);
+      for (int u = 0; u < kUnroll; ++u)
+        if (v + u * NT < v1) d[u] = load16(vp + v + u * NT);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float m = E::vmax(d[u]);
-      if (m > best) {
-        best = m;
-        bestv = v + u * kThreads;
-        bestd = d[u];
+      for (int u = 0; u < kUnroll; ++u) {
+        if (v + u * NT < v1) {
+          const float m = E::vmax(d[u]);
+          if (m > best) {
+            best = m;
+            bestv = v + u * NT;
+            bestd = d[u];
+          }
+        }
       }
     }
-  }
-  for (; v < v1; v += kThreads) {
-    const u32x4 d = load16(vp + v);
-    const float m = E::vmax(d);
-    if (m > best) {
-      best = m;
-      bestv = v;
-      bestd = d;
+  } else {
+    int v = v0 + tid;
+    for (; v + (kUnroll - 1) * NT < v1; v += kUnroll * NT) {
+      u32x4 d[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) d[u] = load16(vp + v + u * NT);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float m = E::vmax(d[u]);
+        if (m > best) {
+          best = m;
+          bestv = v + u * NT;
+          bestd = d[u];
+        }
+      }
+    }
+    for (; v < v1; v += NT) {
+      const u32x4 d = load16(vp + v);
+      const float m = E::vmax(d);
+      if (m > best) {
+        best = m;
+        bestv = v;
+        bestd = d;
+      }
     }
   }
 
@@ -98,8 +127,8 @@ __device__ inline void sweep_chunk(int blk, const unsigned char* __restrict__ lo
     const int oi = __shfl_xor(idx, off);
     take_better(best, idx, ov, oi);
   }
-  __shared__ float sv[kWaves];
-  __shared__ int si[kWaves];
+  __shared__ float sv[kW];
+  __shared__ int si[kW];
   const int lane = tid & 63, wave = tid >> 6;
   if (lane == 0) {
     sv[wave] = best;
@@ -110,9 +139,11 @@ __device__ inline void sweep_chunk(int blk, const unsigned char* __restrict__ lo
     float bv = sv[0];
     int bi = si[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) take_better(bv, bi, sv[w], si[w]);
+    for (int w = 1; w < kW; ++w) take_better(bv, bi, sv[w], si[w]);
     part[blk] = Partial{bv, bi};
+    return Partial{bv, bi};
   }
+  return Partial{best, idx};
 }
 
 }  // namespace wf

@@ -133,6 +133,29 @@ int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int3
                               int32_t* accept_len, int32_t* bonus, int32_t* row_argmax,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes whiflash_verify_chain_early_exit needs (host-only; 0 when
+ * B <= 0, K < 0 or V <= 0). */
+size_t whiflash_early_exit_workspace_bytes(int32_t B, int32_t K, int32_t V);
+
+/*
+ * DFlash chain verification that reads only the rows it needs (WhiFlash
+ * paper, section 3.2: decoding continues from the last accepted token, so the
+ * rows after the first rejected draft affect neither AL nor the bonus token).
+ * Arguments, layouts, data rules and errors are those of whiflash_verify_chain,
+ * and accept_len and bonus are identical to its results.  row_argmax (when not
+ * NULL) holds t for rows 0..n of each sequence and -1 for the rows after n.
+ * Rows of a sequence after its first mismatch may be skipped in whole or in
+ * part, so the logits bytes read depend on the data (at least rows 0..n).
+ * Workspace: whiflash_early_exit_workspace_bytes(B, K, V) bytes, 256-byte
+ * aligned; it holds per-sequence flags that the call clears itself, so two
+ * calls that share a workspace must not overlap in time.
+ */
+int32_t whiflash_verify_chain_early_exit(const void* logits, int32_t dtype, int32_t B, int32_t K,
+                                         int32_t V, int64_t row_stride, const int32_t* draft,
+                                         int32_t* accept_len, int32_t* bonus, int32_t* row_argmax,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
 /*
  * Greedy verification of EAGLE-3 draft trees with the draft-to-target map
  * (WhiFlash paper, section 3.2: a tree of candidate tokens is verified;

@@ -148,3 +148,27 @@ def test_route_gather_validation():
     assert f(*bad) == -2
     bad = list(ok); bad[17] = 64
     assert f(*bad) == -5
+
+
+def test_verify_chain_early_exit_validation():
+    f = wf.whiflash_verify_chain_early_exit
+    ok = [ALIGNED, 1, 256, 16, V, V, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 1 << 24, None]
+    bad = list(ok); bad[6] = None
+    assert f(*bad) == -1
+    bad = list(ok); bad[3] = 1024
+    assert f(*bad) == -2
+    bad = list(ok); bad[5] = V - 8
+    assert f(*bad) == -2
+    bad = list(ok); bad[1] = 7
+    assert f(*bad) == -3
+    bad = list(ok); bad[0] = ALIGNED + 8
+    assert f(*bad) == -4
+    bad = list(ok); bad[11] = wf.early_exit_workspace_bytes(256, 16, V) - 1
+    assert f(*bad) == -5
+    bad = list(ok); bad[10] = ALIGNED + 64
+    assert f(*bad) == -5
+    bad = list(ok); bad[2] = 0
+    assert f(*bad) == 0
+    n = wf.early_exit_workspace_bytes(256, 16, V)
+    assert n % 256 == 0 and n >= 256 * 4 + 256 * 17 * 8
+    assert wf.early_exit_workspace_bytes(0, 16, V) == 0 and wf.early_exit_workspace_bytes(4, -1, V) == 0
