@@ -45,11 +45,12 @@ def _parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", choices=["routed", "sweep"], default="routed")
-    p.add_argument("--pool", type=int, default=4, help="distinct rounds resident in HBM (sweep)")
+    p.add_argument("--pool", type=int, default=4, help="distinct rounds resident in HBM (sweep workload; routed early-exit)")
     p.add_argument("--mode", choices=["fused", "separate", "early-exit"], default="fused",
-                   help="routed workload: whiflash_round_routed, or whiflash_route then "
-                        "whiflash_verify_routed; sweep workload: early-exit verifies with "
-                        "whiflash_verify_chain_early_exit (reads rows 0..n only)")
+                   help="routed workload: whiflash_round_routed, whiflash_route then "
+                        "whiflash_verify_routed, or whiflash_round_routed_early_exit over a pool "
+                        "of --pool rounds; sweep workload: early-exit verifies with "
+                        "whiflash_verify_chain_early_exit (rows up to the first mismatch only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -89,8 +90,12 @@ def _traffic(workload: str, launches_bytes: float):
 class Routed:
     name = "routed_bf16"
 
-    def __init__(self, torch, dev):
-        from synth import make_config
+    def __init__(self, torch, dev, pool=1):
+        """Round 0 is the seeded routed workload itself.  With pool > 1, rounds 1.. keep its
+        router, layout and d2t table and draw fresh drafts and planted tokens (same generator,
+        next round index), with their logits generated on the device."""
+        from synth import make_config, make_routed_batch
+        from synth.workloads import CONFIGS, PLANT_BOOST
         import drafter_routing_verification_amd as wf
         t0 = time.time()
         batch, r = make_config(3)
@@ -100,9 +105,21 @@ class Routed:
         self.hidden, self.W1, self.W2 = T(r.hidden), T(r.W1), T(r.W2)
         self.b1 = T(r.b1)
         self.b2 = torch.tensor([r.b2], dtype=torch.float32, device=dev)
-        self.logits = T(batch.logits)
-        self.offsets, self.chain_draft = T(batch.offsets), T(batch.chain_draft)
-        self.parent, self.draft_ids, self.d2t = T(batch.parent), T(batch.draft_ids), T(batch.d2t)
+        self.offsets, self.d2t = T(batch.offsets), T(batch.d2t)
+        self.pool = [dict(logits=T(batch.logits), chain_draft=T(batch.chain_draft),
+                          parent=T(batch.parent), draft_ids=T(batch.draft_ids))]
+        c = CONFIGS[3]
+        g = torch.Generator(device=dev)
+        for rnd in range(1, pool):
+            rb = make_routed_batch(c["seed"], batch.layout_choice, c["K"], c["N"], self.V,
+                                   batch.d2t.shape[0], "bf16", 0.8, 0.7, rnd, logits=False)
+            g.manual_seed(c["seed"] * 1_000_003 + rnd)
+            x = torch.randn((self.rows, self.V), generator=g, device=dev, dtype=torch.float32)
+            planted = torch.from_numpy(np.concatenate(rb.planted).astype(np.int64)).to(dev)
+            x[torch.arange(self.rows, device=dev), planted] += PLANT_BOOST
+            self.pool.append(dict(logits=x.to(torch.bfloat16), chain_draft=T(rb.chain_draft),
+                                  parent=T(rb.parent), draft_ids=T(rb.draft_ids)))
+            del x
         B = self.B
         self.dal = torch.empty(B, dtype=torch.float32, device=dev)
         self.choice = torch.empty(B, dtype=torch.int32, device=dev)
@@ -114,6 +131,12 @@ class Routed:
                                device=dev)
         self.fws = torch.empty(wf.round_workspace_bytes(B, r.m, self.rows, self.V),
                                dtype=torch.uint8, device=dev)
+        K, N = batch.K, batch.N
+        self.ews = torch.empty(wf.routed_early_exit_workspace_bytes(B, K, N, self.rows, self.V),
+                               dtype=torch.uint8, device=dev)
+        self.efws = torch.empty(wf.round_early_exit_workspace_bytes(B, r.m, K, N, self.rows, self.V),
+                                dtype=torch.uint8, device=dev)
+        self.early = False
         self.wf = wf
         self.setup_s = time.time() - t0
         esz = 2
@@ -122,24 +145,38 @@ class Routed:
         meta = (batch.offsets.size + B * batch.K + 2 * B * batch.N + batch.d2t.size + 5 * B) * 4
         self.step_bytes = self.logits_bytes + self.router_bytes + meta
 
+    def use_early_exit(self):
+        """Verify with the early-exit schedule; the bytes a round needs are those of the rows
+        of its accepted nodes (the sum of accept lengths: sibling tokens are distinct, so the
+        accepted nodes form one path), averaged over the pool."""
+        self.early = True
+        self.route(0)
+        need = []
+        for i in range(len(self.pool)):
+            self.verify(i)
+            need.append(int(self.al.sum().item()) * self.V * 2)
+        self.needed_bytes = sum(need) / len(need)
+
     def route(self, i):
         r = self.router
         self.wf.route(self.hidden, self.W1, self.b1, self.W2, self.b2, r.tau, delta_al=self.dal,
                       choice=self.choice, workspace=self.rws)
 
     def verify(self, i):
-        self.wf.verify_routed(self.logits, self.offsets, self.rows, self.choice, self.chain_draft,
-                              self.parent, self.draft_ids, self.d2t, row_argmax=False,
-                              accept_len=self.al, bonus=self.bonus, best_node=self.best,
-                              workspace=self.vws)
+        p = self.pool[i % len(self.pool)]
+        fn = self.wf.verify_routed_early_exit if self.early else self.wf.verify_routed
+        fn(p["logits"], self.offsets, self.rows, self.choice, p["chain_draft"], p["parent"],
+           p["draft_ids"], self.d2t, row_argmax=False, accept_len=self.al, bonus=self.bonus,
+           best_node=self.best, workspace=self.ews if self.early else self.vws)
 
     def fused_step(self, i):
         r = self.router
-        self.wf.round_routed(self.hidden, self.W1, self.b1, self.W2, self.b2, r.tau, self.logits,
-                             self.offsets, self.rows, self.chain_draft, self.parent,
-                             self.draft_ids, self.d2t, row_argmax=False, delta_al=self.dal,
-                             choice=self.choice, accept_len=self.al, bonus=self.bonus,
-                             best_node=self.best, workspace=self.fws)
+        p = self.pool[i % len(self.pool)]
+        fn = self.wf.round_routed_early_exit if self.early else self.wf.round_routed
+        fn(self.hidden, self.W1, self.b1, self.W2, self.b2, r.tau, p["logits"], self.offsets,
+           self.rows, p["chain_draft"], p["parent"], p["draft_ids"], self.d2t, row_argmax=False,
+           delta_al=self.dal, choice=self.choice, accept_len=self.al, bonus=self.bonus,
+           best_node=self.best, workspace=self.efws if self.early else self.fws)
 
     def check(self):
         al = self.al.cpu().numpy()
@@ -282,17 +319,18 @@ def main():
     import torch
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    work = Routed(torch, dev) if args.workload == "routed" else Sweep(torch, dev, args.pool)
+    if args.workload == "routed":
+        work = Routed(torch, dev, args.pool if args.mode == "early-exit" else 1)
+    else:
+        work = Sweep(torch, dev, args.pool)
     stream = torch.cuda.current_stream()
     print(f"# workload {work.name}: inputs resident in HBM ({work.setup_s:.1f} s setup)",
           file=sys.stderr, flush=True)
 
-    fused = args.mode == "fused" and hasattr(work, "fused_step")
     early = args.mode == "early-exit"
+    # The routed workload's early-exit step is the fused round; the chain workload has none.
+    fused = args.mode in ("fused", "early-exit") and hasattr(work, "fused_step")
     if early:
-        if not hasattr(work, "use_early_exit"):
-            print("--mode early-exit applies to the chain-only sweep workload", file=sys.stderr)
-            sys.exit(2)
         work.use_early_exit()
 
     def step(i):
@@ -342,7 +380,8 @@ def main():
     alg_bytes = work.needed_bytes if early else work.logits_bytes
     achieved = alg_bytes / verify_s / 1e9
     traffic = None if early else _traffic(work.name, work.logits_bytes)
-    mode = ("whiflash_round_routed" if fused else
+    mode = ("whiflash_round_routed_early_exit" if fused and early else
+            "whiflash_round_routed" if fused else
             "whiflash_route + whiflash_verify_chain_early_exit" if early else
             "whiflash_route + whiflash_verify_*")
     out = {
@@ -369,8 +408,8 @@ def main():
         "mean_accept_len": round(mean_al, 3),
         **({"logits_bytes_needed_per_round": round(alg_bytes)} if early else {}),
         "roofline": {
-            "kernel": ("whiflash_verify_chain_early_exit call: flag clear + early-exit sweep + "
-                       "acceptance, back to back; bytes = rows 0..n" if early else
+            "kernel": ("whiflash_verify_*_early_exit call: preparation + early-exit sweep + "
+                       "acceptance, back to back; bytes = rows of accepted nodes" if early else
                        "whiflash_verify_* call: argmax sweep + acceptance kernel, back to back"),
             "bound": "hbm",
             "achieved": round(achieved, 1),

@@ -11,6 +11,9 @@ Entry points (same names as the C ABI):
                                                           -> (delta_al, choice)
     verify_chain(logits, draft)                           -> (accept_len, bonus, row_argmax)
     verify_chain_early_exit(logits, draft)                -> (accept_len, bonus, row_argmax)
+    verify_tree_early_exit, verify_routed_early_exit, round_routed_early_exit: same arguments
+        and results as verify_tree, verify_routed, round_routed; only the rows of accepted
+        nodes are read, and row_argmax is -1 for the others
     verify_tree(logits, parent, draft_ids, d2t)           -> (accept_len, bonus, best_node, row_argmax)
     verify_routed(logits, row_offsets, total_rows, choice, chain_draft, parent, draft_ids, d2t)
                                                           -> (accept_len, bonus, best_node, row_argmax)
@@ -37,6 +40,15 @@ from ._binding import (  # noqa: F401
     verify_chain,
     verify_tree,
     verify_chain_early_exit,
+    verify_tree_early_exit,
+    verify_routed_early_exit,
+    round_routed_early_exit,
+    tree_early_exit_workspace_bytes,
+    routed_early_exit_workspace_bytes,
+    round_early_exit_workspace_bytes,
+    whiflash_verify_tree_early_exit,
+    whiflash_verify_routed_early_exit,
+    whiflash_round_routed_early_exit,
     early_exit_workspace_bytes,
     whiflash_verify_chain_early_exit,
     verify_routed,

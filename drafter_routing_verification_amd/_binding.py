@@ -32,6 +32,22 @@ _SIGNATURES = {
     "whiflash_early_exit_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32]),
     "whiflash_verify_chain_early_exit": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p,
                                                   _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "whiflash_tree_early_exit_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32]),
+    "whiflash_verify_tree_early_exit": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p,
+                                                 _c_p, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                 _c_sz, _c_p]),
+    "whiflash_routed_early_exit_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "whiflash_verify_routed_early_exit": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_i32,
+                                                   _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p,
+                                                   _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz,
+                                                   _c_p]),
+    "whiflash_round_early_exit_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                          _c_i32]),
+    "whiflash_round_routed_early_exit": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p,
+                                                  _c_f, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                                  _c_i64, _c_p, _c_i32, _c_i32, _c_p, _c_i32, _c_p,
+                                                  _c_p, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                  _c_sz, _c_p]),
     "whiflash_verify_tree": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
                                       _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_route_gather": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p,
@@ -103,6 +119,30 @@ def whiflash_verify_chain_early_exit(*args):
 
 def early_exit_workspace_bytes(B: int, K: int, V: int) -> int:
     return int(lib().whiflash_early_exit_workspace_bytes(B, K, V))
+
+
+def whiflash_verify_tree_early_exit(*args):
+    return lib().whiflash_verify_tree_early_exit(*args)
+
+
+def whiflash_verify_routed_early_exit(*args):
+    return lib().whiflash_verify_routed_early_exit(*args)
+
+
+def whiflash_round_routed_early_exit(*args):
+    return lib().whiflash_round_routed_early_exit(*args)
+
+
+def tree_early_exit_workspace_bytes(B: int, N: int, V: int) -> int:
+    return int(lib().whiflash_tree_early_exit_workspace_bytes(B, N, V))
+
+
+def routed_early_exit_workspace_bytes(B: int, K: int, N: int, total_rows: int, V: int) -> int:
+    return int(lib().whiflash_routed_early_exit_workspace_bytes(B, K, N, total_rows, V))
+
+
+def round_early_exit_workspace_bytes(B: int, m: int, K: int, N: int, total_rows: int, V: int) -> int:
+    return int(lib().whiflash_round_early_exit_workspace_bytes(B, m, K, N, total_rows, V))
 
 
 def whiflash_verify_tree(*args):
@@ -323,7 +363,7 @@ def verify_chain_early_exit(logits, draft, *, row_argmax=True, accept_len=None, 
 
 
 def verify_tree(logits, parent, draft_ids, d2t, *, row_argmax=True, accept_len=None, bonus=None,
-                best_node=None, workspace=None, stream=None):
+                best_node=None, workspace=None, stream=None, _early=False):
     """EAGLE-3 tree verification.  logits [B*N, V] or [B, N, V]; parent, draft_ids [B, N] int32;
     d2t [Vd] int32."""
     _device_tensor(parent, "parent")
@@ -341,8 +381,10 @@ def verify_tree(logits, parent, draft_ids, d2t, *, row_argmax=True, accept_len=N
         row_argmax = torch.empty(rows, dtype=torch.int32, device=dev)
     elif row_argmax is False:
         row_argmax = None
-    ws = _workspace(workspace, verify_workspace_bytes(rows, V), dev)
-    _check(whiflash_verify_tree(_ptr(logits), _dtype_code(logits), B, N, V, stride, _ptr(parent),
+    nbytes = tree_early_exit_workspace_bytes(B, N, V) if _early else verify_workspace_bytes(rows, V)
+    ws = _workspace(workspace, nbytes, dev)
+    fn = whiflash_verify_tree_early_exit if _early else whiflash_verify_tree
+    _check(fn(_ptr(logits), _dtype_code(logits), B, N, V, stride, _ptr(parent),
                                 _ptr(draft_ids), _ptr(d2t), d2t.numel(), _ptr(accept_len),
                                 _ptr(bonus), _ptr(best_node), _ptr(row_argmax), _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(),
@@ -352,7 +394,7 @@ def verify_tree(logits, parent, draft_ids, d2t, *, row_argmax=True, accept_len=N
 
 def verify_routed(logits, row_offsets, total_rows: int, choice, chain_draft, parent, draft_ids, d2t,
                   *, row_argmax=True, accept_len=None, bonus=None, best_node=None, workspace=None,
-                  stream=None):
+                  stream=None, _early=False):
     """Routed ragged batch.  logits [total_rows, V] packed; row_offsets [B+1], choice [B],
     chain_draft [B, K], parent and draft_ids [B, N], d2t [Vd] -- all int32 device tensors."""
     _device_tensor(choice, "choice")
@@ -376,8 +418,11 @@ def verify_routed(logits, row_offsets, total_rows: int, choice, chain_draft, par
         row_argmax = torch.empty(max(total_rows, 1), dtype=torch.int32, device=dev)
     elif row_argmax is False:
         row_argmax = None
-    ws = _workspace(workspace, verify_workspace_bytes(total_rows, V), dev)
-    _check(whiflash_verify_routed(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(row_offsets),
+    nbytes = (routed_early_exit_workspace_bytes(B, K, N, total_rows, V) if _early
+              else verify_workspace_bytes(total_rows, V))
+    ws = _workspace(workspace, nbytes, dev)
+    fn = whiflash_verify_routed_early_exit if _early else whiflash_verify_routed
+    _check(fn(_ptr(logits), _dtype_code(logits), B, V, stride, _ptr(row_offsets),
                                   total_rows, _ptr(choice), K, _ptr(chain_draft), N, _ptr(parent),
                                   _ptr(draft_ids), _ptr(d2t), d2t.numel(), _ptr(accept_len),
                                   _ptr(bonus), _ptr(best_node), _ptr(row_argmax), _ptr(ws),
@@ -442,7 +487,7 @@ def catchup_update(cur_choice, accept_len, next_choice, backlog, *, switch_flag=
 def round_routed(hidden, W1, b1, W2, b2, tau: float, logits, row_offsets, total_rows: int,
                  chain_draft, parent, draft_ids, d2t, *, row_argmax=True, delta_al=None,
                  choice=None, accept_len=None, bonus=None, best_node=None, workspace=None,
-                 stream=None):
+                 stream=None, _early=False):
     """route + verify_routed in one call (three launches).  Returns
     (delta_al, choice, accept_len, bonus, best_node, row_argmax)."""
     _device_tensor(hidden, "hidden")
@@ -479,8 +524,11 @@ def round_routed(hidden, W1, b1, W2, b2, tau: float, logits, row_offsets, total_
         row_argmax = torch.empty(max(total_rows, 1), dtype=torch.int32, device=dev)
     elif row_argmax is False:
         row_argmax = None
-    ws = _workspace(workspace, round_workspace_bytes(B, m, total_rows, V), dev)
-    _check(whiflash_round_routed(_ptr(hidden), _dtype_code(hidden), d, _ptr(W1), _ptr(b1), m,
+    nbytes = (round_early_exit_workspace_bytes(B, m, K, N, total_rows, V) if _early
+              else round_workspace_bytes(B, m, total_rows, V))
+    ws = _workspace(workspace, nbytes, dev)
+    fn = whiflash_round_routed_early_exit if _early else whiflash_round_routed
+    _check(fn(_ptr(hidden), _dtype_code(hidden), d, _ptr(W1), _ptr(b1), m,
                                  _ptr(W2), _ptr(b2), float(tau), _ptr(delta_al), _ptr(choice),
                                  _ptr(logits), _dtype_code(logits), B, V, stride, _ptr(row_offsets),
                                  total_rows, K, _ptr(chain_draft), N, _ptr(parent), _ptr(draft_ids),
@@ -489,3 +537,22 @@ def round_routed(hidden, W1, b1, W2, b2, tau: float, logits, row_offsets, total_
                                  0 if ws is None else ws.numel() * ws.element_size(),
                                  _stream(hidden, stream)))
     return delta_al, choice, accept_len, bonus, best_node, row_argmax
+
+
+def verify_tree_early_exit(logits, parent, draft_ids, d2t, **kw):
+    """verify_tree that reads only the rows of accepted nodes (row_argmax -1 elsewhere)."""
+    return verify_tree(logits, parent, draft_ids, d2t, _early=True, **kw)
+
+
+def verify_routed_early_exit(logits, row_offsets, total_rows: int, choice, chain_draft, parent,
+                             draft_ids, d2t, **kw):
+    """verify_routed that reads only the rows of accepted nodes (row_argmax -1 elsewhere)."""
+    return verify_routed(logits, row_offsets, total_rows, choice, chain_draft, parent, draft_ids, d2t,
+                         _early=True, **kw)
+
+
+def round_routed_early_exit(hidden, W1, b1, W2, b2, tau: float, logits, row_offsets, total_rows: int,
+                            chain_draft, parent, draft_ids, d2t, **kw):
+    """round_routed with the early-exit verification (four launches)."""
+    return round_routed(hidden, W1, b1, W2, b2, tau, logits, row_offsets, total_rows, chain_draft,
+                        parent, draft_ids, d2t, _early=True, **kw)

@@ -234,6 +234,7 @@ __device__ inline void tree_accept(const TreeIn& in, const int* t_s, int N, int*
 struct AcceptLds {
   int t_s[kMaxSeqRows], anc[kMaxSeqRows], dep[kMaxSeqRows], ok[kMaxSeqRows];
   int red[kWaves];
+  int best;
 };
 
 // Arguments of the routed dispatch (see whiflash_verify_routed).
@@ -252,6 +253,9 @@ struct RoutedArgs {
   int32_t* bonus;
   int32_t* best_node;
   int32_t* row_argmax;
+  // Early-exit schedule: only the rows of accepted nodes were read whole, so
+  // row_argmax gets t for those rows and -1 for the others.
+  bool early = false;
 };
 
 // Loads of sequence b of a routed batch that depend on nothing else.  The
@@ -289,22 +293,36 @@ __device__ inline void routed_accept(const RoutedIn& in, const RoutedArgs& a, in
   const int rows = in.hi - in.lo;
   const bool chain = in_range && c == 0 && rows == a.K + 1;
   const bool tree = in_range && c == 1 && rows == a.N;
-  if (in_range) merge_finish(in.merge, a.part, a.splits, in.lo, rows, L.t_s, a.row_argmax);
+  if (in_range)
+    merge_finish(in.merge, a.part, a.splits, in.lo, rows, L.t_s, a.early ? nullptr : a.row_argmax);
   if (!chain && !tree) {
     if (threadIdx.x == 0) {
       a.accept_len[b] = 0;
       a.bonus[b] = -1;
       if (a.best_node) a.best_node[b] = -1;
     }
+    if (a.early && a.row_argmax && in_range)
+      for (int i = threadIdx.x; i < rows; i += kThreads) a.row_argmax[in.lo + i] = -1;
     return;
   }
   __syncthreads();
+  int32_t* best_out = a.early ? &L.best : (a.best_node ? a.best_node + b : nullptr);
   if (chain) {
     chain_accept(in.draft0, L.t_s, a.K, a.chain_draft + static_cast<int64_t>(b) * a.K,
-                 a.accept_len + b, a.bonus + b, a.best_node ? a.best_node + b : nullptr);
+                 a.accept_len + b, a.bonus + b, best_out);
   } else {
     tree_accept(in.tree, L.t_s, a.N, L.anc, L.dep, L.ok, L.red, a.accept_len + b, a.bonus + b,
-                a.best_node ? a.best_node + b : nullptr);
+                best_out);
+  }
+  if (!a.early) return;
+  __syncthreads();
+  const int best = L.best;
+  if (threadIdx.x == 0 && a.best_node) a.best_node[b] = best;
+  if (a.row_argmax) {
+    for (int i = threadIdx.x; i < rows; i += kThreads) {
+      const bool accepted = chain ? i <= best : L.ok[i] != 0;
+      a.row_argmax[in.lo + i] = accepted ? L.t_s[i] : -1;
+    }
   }
 }
 

@@ -229,10 +229,23 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
   wf::Partial* part = static_cast<wf::Partial*>(workspace);
   if (wf::launch_sweep(logits, dtype, row_stride, total_rows, V, plan, part, stream) != hipSuccess)
     return WF_ERR_LAUNCH;
-  return launch_status(wf::launch_finalize_routed(part, plan.splits, B, V, row_offsets, total_rows,
+  return launch_status(wf::launch_finalize_routed(false, part, plan.splits, B, V, row_offsets, total_rows,
                                                   choice, K, chain_draft, N, parent, draft_ids, d2t,
                                                   Vd, accept_len, bonus, best_node, row_argmax,
                                                   stream));
+}
+
+size_t whiflash_tree_early_exit_workspace_bytes(int32_t B, int32_t N, int32_t V) {
+  if (B <= 0 || N <= 0 || N > WHIFLASH_MAX_SEQ_ROWS || V <= 0) return 0;
+  return wf::ee_tree_workspace(B, N, B * N, V, kWorkspaceAlign).total;
+}
+
+size_t whiflash_routed_early_exit_workspace_bytes(int32_t B, int32_t K, int32_t N, int32_t total_rows,
+                                                  int32_t V) {
+  if (B <= 0 || K < 0 || N <= 0 || total_rows < 0 || V <= 0) return 0;
+  const int32_t rmax = K + 1 > N ? K + 1 : N;
+  if (rmax > WHIFLASH_MAX_SEQ_ROWS) return 0;
+  return wf::ee_tree_workspace(B, rmax, total_rows, V, kWorkspaceAlign).total;
 }
 
 size_t whiflash_round_workspace_bytes(int32_t B, int32_t m, int32_t total_rows, int32_t V) {
@@ -320,6 +333,153 @@ int32_t whiflash_route_entropy(const void* logits, int32_t dtype, int32_t total_
   return launch_status(wf::launch_entropy(logits, dtype, row_stride, total_rows, V, B, row0,
                                           rows_per_seq, pos, tau, entropy, choice, workspace,
                                           stream));
+}
+
+size_t whiflash_round_early_exit_workspace_bytes(int32_t B, int32_t m, int32_t K, int32_t N,
+                                                 int32_t total_rows, int32_t V) {
+  if (B <= 0 || m <= 0 || V <= 0) return 0;
+  const size_t ee = whiflash_routed_early_exit_workspace_bytes(B, K, N, total_rows, V);
+  return ee == 0 ? 0 : whiflash_route_workspace_bytes(B, m) + ee;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared body of the early-exit tree / routed entry points: prep (or the
+// round's router finish + prep), node-major sweep, masked routed acceptance.
+// `zp` non-NULL means a fused round whose router stage 1 is already launched.
+int32_t ee_tree_impl(const void* logits, int32_t dtype, int32_t B, int32_t V, int64_t row_stride,
+                     const int32_t* row_offsets, int32_t total_rows, const int32_t* choice,
+                     int32_t K, const int32_t* chain_draft, int32_t N, const int32_t* parent,
+                     const int32_t* draft_ids, const int32_t* d2t, int32_t Vd, int32_t* accept_len,
+                     int32_t* bonus, int32_t* best_node, int32_t* row_argmax, char* ws,
+                     hipStream_t stream, const wf::RouterPlan* rplan, int32_t hidden_dtype,
+                     const float* zp, int32_t m, const float* b1, const void* W2, const float* b2,
+                     float tau, float* delta_al, int32_t* route_choice) {
+  const int32_t rmax = row_offsets ? (K + 1 > N ? K + 1 : N) : N;
+  const wf::EeTreeWs off = wf::ee_tree_workspace(B, rmax, total_rows, V, kWorkspaceAlign);
+  const wf::SweepPlan plan = wf::early_exit_plan(B, V);
+  const wf::EeTreeArgs a = wf::ee_tree_args(ws, off, B, rmax, logits, dtype, row_stride, V,
+                                            row_offsets, row_offsets ? choice : nullptr,
+                                            total_rows, K, chain_draft, N, parent, draft_ids, d2t,
+                                            Vd);
+  wf::Partial* part = reinterpret_cast<wf::Partial*>(ws + off.part);
+  hipError_t e = rplan ? wf::launch_ee_round_prep(a, hidden_dtype, *rplan, zp, m, b1, W2, b2, tau,
+                                                  delta_al, route_choice, stream)
+                       : wf::launch_ee_tree_prep(a, stream);
+  if (e != hipSuccess) return WF_ERR_LAUNCH;
+  if (wf::launch_ee_tree_sweep(a, plan, part, stream) != hipSuccess) return WF_ERR_LAUNCH;
+  const int32_t* offs = row_offsets ? row_offsets : a.seq_off;
+  const int32_t* ch = row_offsets ? choice : a.seq_choice;
+  const int32_t rows_total = row_offsets ? total_rows : B * N;
+  return launch_status(wf::launch_finalize_routed(true, part, plan.splits, B, V, offs, rows_total, ch,
+                                                  row_offsets ? K : 0, chain_draft, N, parent,
+                                                  draft_ids, d2t, Vd, accept_len, bonus, best_node,
+                                                  row_argmax, stream));
+}
+
+// Grid of the node-major sweep: rmax * B * splits workgroups of up to 1024 threads.
+bool ee_grid_ok(int32_t B, int32_t rmax, int32_t V) {
+  const wf::SweepPlan plan = wf::early_exit_plan(B, V);
+  return static_cast<int64_t>(rmax) * B * plan.splits * 1024 < (int64_t{1} << 32);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t whiflash_verify_tree_early_exit(const void* logits, int32_t dtype, int32_t B, int32_t N,
+                                        int32_t V, int64_t row_stride, const int32_t* parent,
+                                        const int32_t* draft_ids, const int32_t* d2t, int32_t Vd,
+                                        int32_t* accept_len, int32_t* bonus, int32_t* best_node,
+                                        int32_t* row_argmax, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || N < 1 || N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1) return WF_ERR_SHAPE;
+  const int64_t rows64 = static_cast<int64_t>(B) * N;
+  if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
+  int32_t s = check_logits(logits, dtype, static_cast<int32_t>(rows64), V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!parent || !draft_ids || !d2t || !accept_len || !bonus) return WF_ERR_NULL;
+  if (!ee_grid_ok(B, N, V)) return WF_ERR_SHAPE;
+  if ((s = check_workspace(workspace, workspace_bytes,
+                           whiflash_tree_early_exit_workspace_bytes(B, N, V))) != WF_OK)
+    return s;
+  return ee_tree_impl(logits, dtype, B, V, row_stride, nullptr, static_cast<int32_t>(rows64),
+                      nullptr, 0, nullptr, N, parent, draft_ids, d2t, Vd, accept_len, bonus,
+                      best_node, row_argmax, static_cast<char*>(workspace), stream, nullptr, 0,
+                      nullptr, 0, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr);
+}
+
+int32_t whiflash_verify_routed_early_exit(const void* logits, int32_t dtype, int32_t B, int32_t V,
+                                          int64_t row_stride, const int32_t* row_offsets,
+                                          int32_t total_rows, const int32_t* choice, int32_t K,
+                                          const int32_t* chain_draft, int32_t N,
+                                          const int32_t* parent, const int32_t* draft_ids,
+                                          const int32_t* d2t, int32_t Vd, int32_t* accept_len,
+                                          int32_t* bonus, int32_t* best_node, int32_t* row_argmax,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  if (B < 0 || total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+      N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
+    return WF_ERR_SHAPE;
+  int32_t s = check_logits(logits, dtype, total_rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!row_offsets || !choice || (K > 0 && !chain_draft) || !parent || !draft_ids || !d2t ||
+      !accept_len || !bonus)
+    return WF_ERR_NULL;
+  if (!ee_grid_ok(B, K + 1 > N ? K + 1 : N, V)) return WF_ERR_SHAPE;
+  if ((s = check_workspace(workspace, workspace_bytes,
+                           whiflash_routed_early_exit_workspace_bytes(B, K, N, total_rows, V))) !=
+      WF_OK)
+    return s;
+  return ee_tree_impl(logits, dtype, B, V, row_stride, row_offsets, total_rows, choice, K,
+                      chain_draft, N, parent, draft_ids, d2t, Vd, accept_len, bonus, best_node,
+                      row_argmax, static_cast<char*>(workspace), stream, nullptr, 0, nullptr, 0,
+                      nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr);
+}
+
+int32_t whiflash_round_routed_early_exit(
+    const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1, const float* b1, int32_t m,
+    const void* W2, const float* b2, float tau, float* delta_al, int32_t* choice,
+    const void* logits, int32_t logits_dtype, int32_t B, int32_t V, int64_t row_stride,
+    const int32_t* row_offsets, int32_t total_rows, int32_t K, const int32_t* chain_draft,
+    int32_t N, const int32_t* parent, const int32_t* draft_ids, const int32_t* d2t, int32_t Vd,
+    int32_t* accept_len, int32_t* bonus, int32_t* best_node, int32_t* row_argmax, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(hidden_dtype)) return WF_ERR_DTYPE;
+  if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
+  if (total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+      N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
+    return WF_ERR_SHAPE;
+  int32_t s = check_logits(logits, logits_dtype, total_rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
+  if (!row_offsets || (K > 0 && !chain_draft) || !parent || !draft_ids || !d2t || !accept_len ||
+      !bonus)
+    return WF_ERR_NULL;
+  if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
+    return WF_ERR_SHAPE;
+  if (!ee_grid_ok(B, K + 1 > N ? K + 1 : N, V)) return WF_ERR_SHAPE;
+  if ((s = check_workspace(workspace, workspace_bytes,
+                           whiflash_round_early_exit_workspace_bytes(B, m, K, N, total_rows, V))) !=
+      WF_OK)
+    return s;
+  const size_t route_bytes = whiflash_route_workspace_bytes(B, m);
+  float* zp = static_cast<float*>(workspace);
+  const wf::HiddenSel direct{nullptr, nullptr, 0, 0};
+  const wf::RouterPlan plan = wf::router_plan(hidden_dtype, B, d, m, hidden, W1);
+  if (wf::launch_router_stage1(plan, hidden, direct, hidden_dtype, B, d, W1, m, zp, stream) !=
+      hipSuccess)
+    return WF_ERR_LAUNCH;
+  return ee_tree_impl(logits, logits_dtype, B, V, row_stride, row_offsets, total_rows, choice, K,
+                      chain_draft, N, parent, draft_ids, d2t, Vd, accept_len, bonus, best_node,
+                      row_argmax, static_cast<char*>(workspace) + route_bytes, stream, &plan,
+                      hidden_dtype, zp, m, b1, W2, b2, tau, delta_al, choice);
 }
 
 }  // extern "C"

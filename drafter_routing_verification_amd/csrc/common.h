@@ -55,6 +55,49 @@ __device__ inline int64_t hidden_row(const HiddenSel& s, int b) {
 hipError_t launch_sweep(const void* logits, int dtype, int64_t row_stride, int32_t rows, int32_t V,
                         SweepPlan plan, Partial* part, hipStream_t stream);
 
+// Early-exit verification of trees and routed batches (see early_exit.hip).
+constexpr int kMaxMaskWords = (kMaxSeqRows + 63) / 64;
+
+struct EeTreeArgs {
+  int B, Rmax, W;              // sequences, rows of the longest sequence, 64-bit mask words
+  const int32_t* row_offsets;  // [B+1] device, or NULL: sequence b at rows [b*N, b*N+N)
+  const int32_t* choice;       // [B] device, or NULL: every sequence is a tree
+  int total_rows, K, N, V, Vd;
+  const int32_t* chain_draft;  // [B, K]
+  const int32_t* parent;       // [B, N]
+  const int32_t* draft_ids;    // [B, N]
+  const int32_t* d2t;          // [Vd]
+  const unsigned char* logits;
+  int64_t row_bytes;
+  int dtype;
+  unsigned long long* mask;    // [B][W] rejected nodes
+  unsigned long long* anc;     // [B][Rmax][W] ancestor-or-self masks
+  int32_t* rowmap;             // [Rmax][B] global row of node u of sequence b, or -1
+  int4* edge;                  // [B][Rmax] (parent, target token, parent-row logit bits, valid)
+  int32_t* seq_off;            // [B+1] written for tree-only batches
+  int32_t* seq_choice;         // [B] written for tree-only batches
+};
+
+// Byte offsets of the regions of an early-exit tree / routed workspace.
+struct EeTreeWs {
+  size_t mask, anc, rowmap, edge, seq_off, seq_choice, part, total;
+};
+
+EeTreeWs ee_tree_workspace(int32_t B, int32_t Rmax, int32_t total_rows, int32_t V, size_t align);
+EeTreeArgs ee_tree_args(char* ws, const EeTreeWs& off, int32_t B, int32_t Rmax, const void* logits,
+                        int dtype, int64_t row_stride, int32_t V, const int32_t* row_offsets,
+                        const int32_t* choice, int32_t total_rows, int32_t K,
+                        const int32_t* chain_draft, int32_t N, const int32_t* parent,
+                        const int32_t* draft_ids, const int32_t* d2t, int32_t Vd);
+hipError_t launch_ee_tree_prep(const EeTreeArgs& a, hipStream_t stream);
+struct RouterPlan;
+hipError_t launch_ee_round_prep(const EeTreeArgs& a, int hidden_dtype, const RouterPlan& plan,
+                                const float* zp, int32_t m, const float* b1, const void* W2,
+                                const float* b2, float tau, float* delta_al, int32_t* choice,
+                                hipStream_t stream);
+hipError_t launch_ee_tree_sweep(const EeTreeArgs& a, SweepPlan plan, Partial* part,
+                                hipStream_t stream);
+
 // Early-exit chain verification: chunk plan, and clear + sweep + accept launches.
 // flags holds B int32 (cleared by the call), part B * (K + 1) * plan.splits partials.
 SweepPlan early_exit_plan(int32_t B, int32_t V);
@@ -72,7 +115,7 @@ hipError_t launch_finalize_tree(const Partial* part, int32_t splits, int32_t B, 
                                 int32_t Vd, int32_t* accept_len, int32_t* bonus, int32_t* best_node,
                                 int32_t* row_argmax, hipStream_t stream);
 
-hipError_t launch_finalize_routed(const Partial* part, int32_t splits, int32_t B, int32_t V,
+hipError_t launch_finalize_routed(bool early, const Partial* part, int32_t splits, int32_t B, int32_t V,
                                   const int32_t* row_offsets, int32_t total_rows,
                                   const int32_t* choice, int32_t K, const int32_t* chain_draft,
                                   int32_t N, const int32_t* parent, const int32_t* draft_ids,

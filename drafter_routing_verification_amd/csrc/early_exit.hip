@@ -22,15 +22,35 @@
 // late or stale read of e only means a chunk that could have been skipped is
 // read.  No fence is needed.  The acceptance kernel scans positions in order,
 // so n and t[n] come out exact; rows after n are reported as -1.
+//
+// Trees and routed batches.  An EAGLE-3 draft tree needs only the rows of its
+// accepted nodes: node u >= 1 is accepted iff its parent p is accepted and its
+// target token equals t[p] (same section: a tree of candidate tokens is
+// verified), and the bonus token is t[best].  A DFlash chain is the tree whose
+// node i + 1 hangs under node i with token draft[i], so one schedule serves
+// both and the routed mix.  A per-sequence prep kernel writes, for every node,
+// its ancestor-or-self bit mask and its edge (parent, target token, and the
+// parent row's logit at that token), and starts each sequence's rejected-node
+// mask with the nodes that can never match.  The sweep launches node-major
+// (every sequence's node 0, then node 1, ...; parents precede children since
+// parent[u] < u).  A chunk is skipped when its node's ancestor mask meets the
+// rejected mask; a chunk whose maximum beats a child's (logit, token) marks
+// that child rejected with an agent-scope atomic or.  Marks only name nodes
+// that are truly not accepted, so accepted rows are always read whole.
+// Skipped chunks write nothing: routed row ranges may overlap, and a row one
+// sequence skips may be read by another.  The routed acceptance then runs on
+// the merged partials as in the full path (rows of nodes that are not
+// accepted never decide anything) and reports -1 for them in row_argmax.
 #include "accept.h"
 #include "common.h"
+#include "router_math.h"
 #include "sweep_body.h"
 
 #ifndef WF_EARLY_EXIT_THREADS
 #define WF_EARLY_EXIT_THREADS 512
 #endif
 #ifndef WF_EARLY_EXIT_CHUNK
-#define WF_EARLY_EXIT_CHUNK (WF_EARLY_EXIT_THREADS * 64)
+#define WF_EARLY_EXIT_CHUNK 51200
 #endif
 
 namespace wf {
@@ -39,12 +59,11 @@ namespace {
 // Threads per sweep workgroup.  Workgroups that find their chunk skipped still
 // cost a dispatch each, so this schedule uses fewer, larger workgroups than the
 // full sweep, each issuing whole batches of loads.  Same-process A/B on 256
-// chains of K = 16 at an 80% match rate (median of 5 trials, whole verify
-// call): 512 threads 83.0 us; 256 threads 93.7 us; 1024 threads 94.9 us; the
-// full sweep's loop form at 256 / 512 threads 99.8 / 102.6 us.
+// chains of K = 16 at an 80% match rate, 5 chunks per row (median of 5
+// trials, whole verify call): 512 threads 83.0 us; 256 threads 93.7 us; 1024
+// threads 94.9 us; the full sweep's loop form at 256 / 512 threads 99.8 /
+// 102.6 us.
 constexpr int kEeThreads = WF_EARLY_EXIT_THREADS;
-// Sweep workgroups resident at once on the 256 compute units (32 waves each).
-constexpr int64_t kEeResident = 256 * (32 * 64 / kEeThreads);
 
 __global__ __launch_bounds__(kThreads) void early_exit_clear_kernel(int* __restrict__ flags, int B) {
   const int i = blockIdx.x * kThreads + threadIdx.x;
@@ -117,21 +136,184 @@ __global__ __launch_bounds__(kThreads) void early_exit_accept_kernel(
     row_argmax[static_cast<int64_t>(b) * R + i] = i <= n ? t_s[i] : -1;
 }
 
+// ----------------------------------------------------------------- trees and routed batches
+
+// Node table of one sequence (prep kernel, one 256-thread workgroup per
+// sequence, c = its drafter choice).  p_s is LDS of kMaxSeqRows ints, mask_s
+// LDS of kMaxMaskWords words.
+__device__ inline void ee_prep_sequence(const EeTreeArgs& a, int b, int c, int* p_s,
+                                        unsigned long long* mask_s) {
+  const int tid = threadIdx.x;
+  const int lo = a.row_offsets ? a.row_offsets[b] : b * a.N;
+  const int hi = a.row_offsets ? a.row_offsets[b + 1] : lo + a.N;
+  const bool in_range = lo >= 0 && lo <= hi && hi <= a.total_rows;
+  const int n = hi - lo;
+  const bool chain = in_range && c == 0 && n == a.K + 1;
+  const bool tree = in_range && c == 1 && n == a.N;
+  const bool ok = chain || tree;
+  for (int u = tid; u < a.Rmax; u += kThreads)
+    a.rowmap[static_cast<int64_t>(u) * a.B + b] = ok && u < n ? lo + u : -1;
+  if (!ok) return;  // malformed: no row of this sequence is read
+  for (int w = tid; w < a.W; w += kThreads) mask_s[w] = 0ull;
+  __syncthreads();
+  const unsigned char* base = a.logits + static_cast<int64_t>(lo) * a.row_bytes;
+  for (int u = tid; u < a.Rmax; u += kThreads) {
+    int p = -1, tok = -1;
+    if (u >= 1 && u < n) {
+      if (chain) {
+        p = u - 1;
+        tok = a.chain_draft[static_cast<int64_t>(b) * a.K + u - 1];
+      } else {
+        p = a.parent[static_cast<int64_t>(b) * a.N + u];
+        const int did = a.draft_ids[static_cast<int64_t>(b) * a.N + u];
+        tok = did >= 0 && did < a.Vd ? a.d2t[did] : -1;
+      }
+    }
+    const bool reach = u >= 1 && u < n && p >= 0 && p < u;
+    const bool valid = reach && tok >= 0 && tok < a.V;
+    if (u < kMaxSeqRows) p_s[u] = reach ? p : -1;
+    if (u >= 1 && u < n && !valid) atomicOr(&mask_s[u >> 6], 1ull << (u & 63));
+    float xv = 0.0f;
+    if (valid) {
+      const unsigned char* rowp = base + static_cast<int64_t>(p) * a.row_bytes;
+      xv = a.dtype == WF_BF16 ? Elem<WF_BF16>::scalar(rowp, tok) : Elem<WF_F32>::scalar(rowp, tok);
+    }
+    a.edge[static_cast<int64_t>(b) * a.Rmax + u] = make_int4(p, tok, __float_as_int(xv), valid ? 1 : 0);
+  }
+  __syncthreads();
+  // Ancestor-or-self masks: a chain's node u has bits 0..u; a tree node walks
+  // its parents (each strictly smaller, so the walk ends at the root or at an
+  // unreachable node).
+  for (int u = tid; u < n; u += kThreads) {
+    for (int w = 0; w < a.W; ++w) {
+      unsigned long long m = 0ull;
+      if (chain) {
+        const int lo_bit = w * 64;
+        if (u >= lo_bit + 63) m = ~0ull;
+        else if (u >= lo_bit) m = (2ull << (u - lo_bit)) - 1ull;
+      } else {
+        for (int v = u; v >= 0; v = p_s[v])
+          if ((v >> 6) == w) m |= 1ull << (v & 63);
+      }
+      a.anc[(static_cast<int64_t>(b) * a.Rmax + u) * a.W + w] = m;
+    }
+  }
+  for (int w = tid; w < a.W; w += kThreads) a.mask[static_cast<int64_t>(b) * a.W + w] = mask_s[w];
+}
+
+__global__ __launch_bounds__(kThreads) void ee_prep_kernel(EeTreeArgs a) {
+  __shared__ int p_s[kMaxSeqRows];
+  __shared__ unsigned long long mask_s[kMaxMaskWords];
+  const int b = blockIdx.x;
+  int c = 1;
+  if (a.choice) {
+    c = a.choice[b];
+  } else if (threadIdx.x == 0) {  // tree-only batch: offsets and choices for the acceptance
+    a.seq_off[b] = b * a.N;
+    if (b == a.B - 1) a.seq_off[a.B] = a.B * a.N;
+    a.seq_choice[b] = 1;
+  }
+  ee_prep_sequence(a, b, c, p_s, mask_s);
+}
+
+// Routed round: finish the router for sequence b (Delta-AL, choice), then
+// prepare the sequence for the drafter it chose.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void ee_round_prep_kernel(
+    EeTreeArgs a, const float* __restrict__ zp, int KS, int m, const float* __restrict__ b1,
+    const void* __restrict__ W2, const float* __restrict__ b2, float tau,
+    float* __restrict__ delta_al, int32_t* __restrict__ choice) {
+  __shared__ int p_s[kMaxSeqRows];
+  __shared__ unsigned long long mask_s[kMaxMaskWords];
+  __shared__ float redf[kWaves];
+  const int b = blockIdx.x;
+  const HiddenSel direct{nullptr, nullptr, 0, 0};
+  FinishIn fin;
+  finish_load_pass<DT>(fin, zp, KS, a.B, m, b, 0, b1, W2);
+  const float dal = router_finish_compute<DT>(fin, zp, direct, KS, a.B, m, b, b1, W2, b2, redf);
+  const int c = dal > tau ? 1 : 0;
+  if (threadIdx.x == 0) {
+    delta_al[b] = dal;
+    choice[b] = c;
+  }
+  ee_prep_sequence(a, b, c, p_s, mask_s);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kEeThreads) void ee_tree_sweep_kernel(EeTreeArgs a, int splits,
+                                                                    int chunk_vecs, int nvec,
+                                                                    Partial* __restrict__ part) {
+  const int per_u = a.B * splits;
+  const int u = blockIdx.x / per_u;
+  const int rem = blockIdx.x - u * per_u;
+  const int b = rem / splits;
+  const int c = rem - b * splits;
+  __shared__ int row_s;
+  __shared__ float bv_s;
+  __shared__ int bi_s;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int row = tid == 0 ? a.rowmap[static_cast<int64_t>(u) * a.B + b] : 0;
+    bool hit = false;
+    if (tid < a.W) {
+      const unsigned long long m = __hip_atomic_load(&a.mask[static_cast<int64_t>(b) * a.W + tid],
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long an = a.anc[(static_cast<int64_t>(b) * a.Rmax + u) * a.W + tid];
+      hit = (m & an) != 0ull;
+    }
+    const bool rejected = __ballot(hit) != 0ull;
+    if (tid == 0) row_s = rejected ? -1 : row;
+  }
+  __syncthreads();
+  const int row = row_s;
+  if (row < 0) return;  // no such node, or not accepted: nothing is written
+  // Edges of this sequence (one per node), consumed after the sweep.
+  const int4* eb = a.edge + static_cast<int64_t>(b) * a.Rmax;
+  const int4 none = make_int4(-1, -1, 0, 0);
+  const int4 e0 = tid < a.Rmax ? eb[tid] : none;
+  const int4 e1 = tid + kEeThreads < a.Rmax ? eb[tid + kEeThreads] : none;
+  const Partial r = sweep_chunk<DT, kEeThreads, true>(row * splits + c, a.logits, a.row_bytes, a.V,
+                                                      splits, chunk_vecs, nvec, part);
+  if (tid == 0) {
+    bv_s = r.val;
+    bi_s = r.idx;
+  }
+  __syncthreads();
+  const float bv = bv_s;
+  const int bi = bi_s;
+  unsigned long long* mb = a.mask + static_cast<int64_t>(b) * a.W;
+  // A child whose (logit, token) is beaten inside this chunk is not the greedy
+  // token of this row, so it is not accepted.
+  if (e0.w && e0.x == u) {
+    const float xv = __int_as_float(e0.z);
+    if (bv > xv || (bv == xv && bi < e0.y))
+      __hip_atomic_fetch_or(&mb[tid >> 6], 1ull << (tid & 63), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (e1.w && e1.x == u) {
+    const int v = tid + kEeThreads;
+    const float xv = __int_as_float(e1.z);
+    if (bv > xv || (bv == xv && bi < e1.y))
+      __hip_atomic_fetch_or(&mb[v >> 6], 1ull << (v & 63), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 }  // namespace
 
 SweepPlan early_exit_plan(int32_t B, int32_t V) {
-  // Chunks of about one batch of 16-byte loads per thread (kEeThreads x 8
-  // vectors of 8 bf16, 5 chunks per 151,936-wide row), starting on
-  // 256-element boundaries.  Measured on 256 chains of K = 16 (whole call):
-  // 4 / 5 / 8 / 10 chunks per row 87.2 / 82.6 / 95.8 / 105.2 us.  Small
-  // batches are split further so that one position has at least as many
-  // workgroups as are resident at once: then a sequence's next row is
-  // dispatched only after its current row's workgroups have mostly finished,
-  // and a mismatch found there is seen.  Chunks stay at least 2048 elements.
-  const int64_t target = WF_EARLY_EXIT_CHUNK;
-  int64_t splits = (V + target - 1) / target;
-  const int64_t for_window = (kEeResident + B - 1) / (B > 0 ? B : 1);
-  if (splits < for_window) splits = for_window;
+  // Chunks of ~51K elements (3 per 151,936-wide row), starting on 256-element
+  // boundaries.  Every chunk of a skipped row still costs a dispatch and a
+  // flag round trip, so few chunks per row pay; too few lengthen each row's
+  // read on the chain of dependent rows.  Measured, whole call, on the routed
+  // workload (128 sequences, 4,992 rows) / the chain workload (256 chains of
+  // K = 16): 1 chunk per row 88.3 / 112.9 us, 2 chunks 72.1 / 87.1 us,
+  // 3 chunks 72.1 / 83.2 us, 5 chunks 79.6 / 83.0 us, 8 chunks (one position's
+  // workgroups filling the resident slots) 100.4 / 82.6 us, 12 chunks 126.3 /
+  // 115.8 us; 1024-thread workgroups over 1 or 2 chunks 77.5-81.0 / 91.0-97.3.
+  (void)B;
+  constexpr int64_t kChunkTarget = WF_EARLY_EXIT_CHUNK;
+  int64_t splits = (V + kChunkTarget - 1) / kChunkTarget;
   const int64_t max_splits = V / 2048 > 1 ? V / 2048 : 1;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -164,6 +346,87 @@ hipError_t launch_early_exit_chain(const void* logits, int dtype, int64_t row_st
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL(early_exit_accept_kernel, dim3(B), dim3(kThreads), 0, stream, part,
                      plan.splits, K, draft, accept_len, bonus, row_argmax);
+  return hipGetLastError();
+}
+
+EeTreeWs ee_tree_workspace(int32_t B, int32_t Rmax, int32_t total_rows, int32_t V, size_t align) {
+  auto up = [align](size_t x) { return (x + align - 1) / align * align; };
+  EeTreeWs w{};
+  const size_t W = static_cast<size_t>((Rmax + 63) / 64);
+  const SweepPlan plan = early_exit_plan(B, V);
+  w.mask = 0;
+  w.anc = w.mask + up(static_cast<size_t>(B) * W * 8);
+  w.rowmap = w.anc + up(static_cast<size_t>(B) * Rmax * W * 8);
+  w.edge = w.rowmap + up(static_cast<size_t>(B) * Rmax * 4);
+  w.seq_off = w.edge + up(static_cast<size_t>(B) * Rmax * 16);
+  w.seq_choice = w.seq_off + up((static_cast<size_t>(B) + 1) * 4);
+  w.part = w.seq_choice + up(static_cast<size_t>(B) * 4);
+  w.total = w.part + up(static_cast<size_t>(total_rows) * plan.splits * sizeof(Partial));
+  return w;
+}
+
+EeTreeArgs ee_tree_args(char* ws, const EeTreeWs& off, int32_t B, int32_t Rmax, const void* logits,
+                        int dtype, int64_t row_stride, int32_t V, const int32_t* row_offsets,
+                        const int32_t* choice, int32_t total_rows, int32_t K,
+                        const int32_t* chain_draft, int32_t N, const int32_t* parent,
+                        const int32_t* draft_ids, const int32_t* d2t, int32_t Vd) {
+  EeTreeArgs a{};
+  a.B = B;
+  a.Rmax = Rmax;
+  a.W = (Rmax + 63) / 64;
+  a.row_offsets = row_offsets;
+  a.choice = choice;
+  a.total_rows = total_rows;
+  a.K = K;
+  a.N = N;
+  a.V = V;
+  a.Vd = Vd;
+  a.chain_draft = chain_draft;
+  a.parent = parent;
+  a.draft_ids = draft_ids;
+  a.d2t = d2t;
+  a.logits = static_cast<const unsigned char*>(logits);
+  a.row_bytes = row_stride * (dtype == WF_BF16 ? 2 : 4);
+  a.dtype = dtype;
+  a.mask = reinterpret_cast<unsigned long long*>(ws + off.mask);
+  a.anc = reinterpret_cast<unsigned long long*>(ws + off.anc);
+  a.rowmap = reinterpret_cast<int32_t*>(ws + off.rowmap);
+  a.edge = reinterpret_cast<int4*>(ws + off.edge);
+  a.seq_off = reinterpret_cast<int32_t*>(ws + off.seq_off);
+  a.seq_choice = reinterpret_cast<int32_t*>(ws + off.seq_choice);
+  return a;
+}
+
+hipError_t launch_ee_tree_prep(const EeTreeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(ee_prep_kernel, dim3(a.B), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ee_round_prep(const EeTreeArgs& a, int hidden_dtype, const RouterPlan& plan,
+                                const float* zp, int32_t m, const float* b1, const void* W2,
+                                const float* b2, float tau, float* delta_al, int32_t* choice,
+                                hipStream_t stream) {
+  if (hidden_dtype == WF_BF16)
+    hipLaunchKernelGGL(ee_round_prep_kernel<WF_BF16>, dim3(a.B), dim3(kThreads), 0, stream, a, zp,
+                       plan.slices, m, b1, W2, b2, tau, delta_al, choice);
+  else
+    hipLaunchKernelGGL(ee_round_prep_kernel<WF_F32>, dim3(a.B), dim3(kThreads), 0, stream, a, zp,
+                       plan.slices, m, b1, W2, b2, tau, delta_al, choice);
+  return hipGetLastError();
+}
+
+hipError_t launch_ee_tree_sweep(const EeTreeArgs& a, SweepPlan plan, Partial* part,
+                                hipStream_t stream) {
+  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.Rmax) * a.B * plan.splits);
+  if (a.dtype == WF_BF16) {
+    using E = Elem<WF_BF16>;
+    hipLaunchKernelGGL(ee_tree_sweep_kernel<WF_BF16>, dim3(blocks), dim3(kEeThreads), 0, stream, a,
+                       plan.splits, plan.chunk / E::kPerVec, a.V / E::kPerVec, part);
+  } else {
+    using E = Elem<WF_F32>;
+    hipLaunchKernelGGL(ee_tree_sweep_kernel<WF_F32>, dim3(blocks), dim3(kEeThreads), 0, stream, a,
+                       plan.splits, plan.chunk / E::kPerVec, a.V / E::kPerVec, part);
+  }
   return hipGetLastError();
 }
 

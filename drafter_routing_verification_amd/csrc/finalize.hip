@@ -80,15 +80,16 @@ hipError_t launch_finalize_tree(const Partial* part, int32_t splits, int32_t B, 
   return hipGetLastError();
 }
 
-hipError_t launch_finalize_routed(const Partial* part, int32_t splits, int32_t B, int32_t V,
+hipError_t launch_finalize_routed(bool early, const Partial* part, int32_t splits, int32_t B, int32_t V,
                                   const int32_t* row_offsets, int32_t total_rows,
                                   const int32_t* choice, int32_t K, const int32_t* chain_draft,
                                   int32_t N, const int32_t* parent, const int32_t* draft_ids,
                                   const int32_t* d2t, int32_t Vd, int32_t* accept_len,
                                   int32_t* bonus, int32_t* best_node, int32_t* row_argmax,
                                   hipStream_t stream) {
-  const RoutedArgs args{part, splits, V, row_offsets, total_rows, K, chain_draft, N, parent,
-                        draft_ids, d2t, Vd, accept_len, bonus, best_node, row_argmax};
+  const RoutedArgs args{part,      splits, V,  row_offsets, total_rows, K,
+                        chain_draft, N,     parent, draft_ids, d2t,   Vd,
+                        accept_len, bonus,  best_node, row_argmax, early};
   hipLaunchKernelGGL(finalize_routed_kernel, dim3(B), dim3(kThreads), 0, stream, args, choice);
   return hipGetLastError();
 }

@@ -285,6 +285,80 @@ int32_t whiflash_route_entropy(const void* logits, int32_t dtype, int32_t total_
                                float* entropy, int32_t* choice,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes of whiflash_verify_tree_early_exit (host-only; 0 on bad sizes). */
+size_t whiflash_tree_early_exit_workspace_bytes(int32_t B, int32_t N, int32_t V);
+
+/*
+ * EAGLE-3 tree verification that reads only the rows it needs (WhiFlash
+ * paper, section 3.2: a tree of candidate tokens is verified and decoding
+ * continues from the deepest accepted node, so only the rows of accepted
+ * nodes decide the acceptance length, the best node and the bonus token).
+ * Arguments, layouts, data rules and errors are those of whiflash_verify_tree,
+ * and accept_len, bonus and best_node are identical to its results.
+ * row_argmax (when not NULL) holds t for the rows of accepted nodes and -1
+ * for every other row.  Rows of nodes that are not accepted may be skipped in
+ * whole or in part.  Workspace: whiflash_tree_early_exit_workspace_bytes(B, N,
+ * V) bytes, 256-byte aligned, contents ignored on entry; two calls that share
+ * a workspace must not overlap in time.
+ */
+int32_t whiflash_verify_tree_early_exit(const void* logits, int32_t dtype, int32_t B, int32_t N,
+                                        int32_t V, int64_t row_stride, const int32_t* parent,
+                                        const int32_t* draft_ids, const int32_t* d2t, int32_t Vd,
+                                        int32_t* accept_len, int32_t* bonus, int32_t* best_node,
+                                        int32_t* row_argmax, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of whiflash_verify_routed_early_exit (host-only; 0 on bad sizes). */
+size_t whiflash_routed_early_exit_workspace_bytes(int32_t B, int32_t K, int32_t N,
+                                                  int32_t total_rows, int32_t V);
+
+/*
+ * Routed verification that reads only the rows it needs: each DFlash chain up
+ * to its first mismatch, each EAGLE-3 tree along its accepted nodes (same
+ * passages as whiflash_verify_chain_early_exit and
+ * whiflash_verify_tree_early_exit).  Arguments, layouts, data rules and errors
+ * are those of whiflash_verify_routed; accept_len, bonus and best_node are
+ * identical to its results (malformed sequences: AL 0, bonus -1, best -1, and
+ * none of their rows are read).  row_argmax (when not NULL) holds t for the
+ * rows of accepted nodes and -1 for the other rows of in-range sequences;
+ * where the row ranges of two sequences overlap, a shared row's entry is
+ * unspecified.  Workspace: whiflash_routed_early_exit_workspace_bytes(B, K, N,
+ * total_rows, V) bytes, 256-byte aligned, contents ignored on entry; calls
+ * sharing a workspace must not overlap in time.
+ */
+int32_t whiflash_verify_routed_early_exit(const void* logits, int32_t dtype, int32_t B, int32_t V,
+                                          int64_t row_stride, const int32_t* row_offsets,
+                                          int32_t total_rows, const int32_t* choice, int32_t K,
+                                          const int32_t* chain_draft, int32_t N,
+                                          const int32_t* parent, const int32_t* draft_ids,
+                                          const int32_t* d2t, int32_t Vd, int32_t* accept_len,
+                                          int32_t* bonus, int32_t* best_node, int32_t* row_argmax,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+/* Workspace bytes of whiflash_round_routed_early_exit (host-only; 0 on bad sizes). */
+size_t whiflash_round_early_exit_workspace_bytes(int32_t B, int32_t m, int32_t K, int32_t N,
+                                                 int32_t total_rows, int32_t V);
+
+/*
+ * One routed round with the early-exit verification: whiflash_route followed
+ * by whiflash_verify_routed_early_exit with the router's choice, in four
+ * launches (router stage 1; router finish + per-sequence preparation; the
+ * node-major sweep; the acceptance).  Arguments and errors are those of
+ * whiflash_round_routed; delta_al, choice, accept_len, bonus and best_node are
+ * those of the two calls made in turn; row_argmax as in
+ * whiflash_verify_routed_early_exit.  Workspace:
+ * whiflash_round_early_exit_workspace_bytes(B, m, K, N, total_rows, V) bytes.
+ */
+int32_t whiflash_round_routed_early_exit(
+    const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1, const float* b1, int32_t m,
+    const void* W2, const float* b2, float tau, float* delta_al, int32_t* choice,
+    const void* logits, int32_t logits_dtype, int32_t B, int32_t V, int64_t row_stride,
+    const int32_t* row_offsets, int32_t total_rows, int32_t K, const int32_t* chain_draft,
+    int32_t N, const int32_t* parent, const int32_t* draft_ids, const int32_t* d2t, int32_t Vd,
+    int32_t* accept_len, int32_t* bonus, int32_t* best_node, int32_t* row_argmax, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

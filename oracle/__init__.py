@@ -23,6 +23,7 @@ from .whiflash import (  # noqa: F401
     route_entropy,
     verify_chain,
     verify_tree,
+    tree_accepted,
     verify_routed,
     catchup_update,
     MALFORMED_AL,

@@ -195,7 +195,16 @@ def verify_chain(t: np.ndarray, draft: np.ndarray):
     return al, bonus
 
 
-def _tree_one(t, parent, draft_ids, d2t, V):
+def tree_accepted(t, parent, draft_ids, d2t, V):
+    """Accepted nodes of one tree, and their depths.
+
+    Same reading as verify_tree ([paper] §3.2; [eagle] "Model Description"):
+    node 0 is accepted at depth 0; in index order, node u >= 1 is accepted iff
+    0 <= parent[u] = p < u, p is accepted, draft_ids[u] lies in the draft
+    vocabulary, its table entry lies in the target vocabulary, and that target
+    id equals t[p]; its depth is then depth[p] + 1.
+    t, parent, draft_ids: int [N]; d2t: int [Vd].  Returns (bool [N], int [N]).
+    """
     N = len(parent)
     Vd = len(d2t)
     accepted = [False] * N
@@ -214,8 +223,13 @@ def _tree_one(t, parent, draft_ids, d2t, V):
         if accepted[p] and tok == int(t[p]):
             accepted[u] = True
             depth[u] = depth[p] + 1
-    best = min((u for u in range(N) if accepted[u]), key=lambda u: (-depth[u], u))
-    return depth[best] + 1, int(t[best]), best
+    return np.array(accepted, bool), np.array(depth, np.int64)
+
+
+def _tree_one(t, parent, draft_ids, d2t, V):
+    accepted, depth = tree_accepted(t, parent, draft_ids, d2t, V)
+    best = min((u for u in range(len(parent)) if accepted[u]), key=lambda u: (-depth[u], u))
+    return int(depth[best]) + 1, int(t[best]), best
 
 
 def verify_tree(t: np.ndarray, parent: np.ndarray, draft_ids: np.ndarray, d2t: np.ndarray, V: int):

@@ -133,6 +133,9 @@ def make_d2t(seed: int, V: int = V_QWEN3, Vd: int = VD_EAGLE3) -> np.ndarray:
 
 
 def _random_tree(g: np.random.Generator, N: int, depth_max: int, children_max: int, Vd: int):
+    if children_max > Vd:
+        # siblings carry distinct draft ids, so a node cannot have more children than ids exist
+        raise ValueError(f"children_max={children_max} exceeds the draft vocabulary Vd={Vd}")
     parent = np.full(N, -1, np.int32)
     depth = np.zeros(N, np.int32)
     nchild = np.zeros(N, np.int32)
@@ -195,6 +198,9 @@ def _tree_sequence(seed: int, rnd: int, b: int, N: int, V: int, d2t: np.ndarray,
 def make_tree_batch(seed: int, B: int, N: int = 61, V: int = V_QWEN3, Vd: int = VD_EAGLE3,
                     dtype: str = "bf16", p_match: float = 0.7, depth_max: int = 8,
                     children_max: int = 10, rnd: int = 0, logits: bool = True) -> TreeBatch:
+    if children_max >= V:
+        # a row whose children's tokens cover the whole vocabulary has no missing token to plant
+        raise ValueError(f"children_max={children_max} must be below the vocabulary V={V}")
     d2t = make_d2t(seed, V, Vd)
     parent = np.empty((B, N), np.int32)
     draft_ids = np.empty((B, N), np.int32)

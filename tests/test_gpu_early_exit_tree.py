@@ -1,0 +1,182 @@
+"""GPU parity of the early-exit tree, routed and fused-round verification
+(whiflash_verify_tree_early_exit, whiflash_verify_routed_early_exit,
+whiflash_round_routed_early_exit) against the oracle.
+
+accept_len, bonus and best_node must equal the oracle's acceptance over the full row
+argmax, bit for bit.  row_argmax must equal the oracle's argmax on the rows of accepted
+nodes (oracle.tree_accepted; for chains the first AL rows) and -1 on every other row of
+an in-range sequence.  Covers random EAGLE-3 trees, deep path-shaped trees whose
+ancestor masks span several 64-bit words, duplicate sibling tokens, malformed parents
+and out-of-domain ids, single-node trees, routed mixes with malformed sequences,
+workspace reuse, and the routed workload at full size through the fused round."""
+
+import numpy as np
+import pytest
+import torch
+
+import drafter_routing_verification_amd as wf
+import oracle
+from gpu_helpers import check_router, dev, host, padded_logits
+from synth import make_config, make_routed_batch, make_tree_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def _stride(V):
+    return (V + 7) // 8 * 8 + 8
+
+
+def _tree_expect(t, parent, ids, d2t, V):
+    B, N = parent.shape
+    al, bo, be = oracle.verify_tree(t.reshape(B, N), parent, ids, d2t, V)
+    rows = np.full(B * N, -1, np.int64)
+    for b in range(B):
+        acc, _ = oracle.tree_accepted(t.reshape(B, N)[b], parent[b], ids[b], d2t, V)
+        rows[b * N:(b + 1) * N] = np.where(acc, t.reshape(B, N)[b], -1)
+    return al, bo, be, rows
+
+
+def _tree_case(B, N, V, Vd, dtype, seed, mutate=None, ws=None, **gen):
+    tb = make_tree_batch(seed, B, N, V, Vd, dtype, **gen)
+    parent, ids, d2t = tb.parent.copy(), tb.draft_ids.copy(), tb.d2t.copy()
+    if mutate:
+        mutate(parent, ids, d2t)
+    out = wf.verify_tree_early_exit(padded_logits(tb.logits, _stride(V)), dev(parent), dev(ids),
+                                    dev(d2t), workspace=ws)
+    torch.cuda.synchronize()
+    al, bo, be, rows = (host(x) for x in out)
+    t = oracle.row_argmax(tb.logits, dtype)
+    e_al, e_bo, e_be, e_rows = _tree_expect(t, parent, ids, d2t, V)
+    assert np.array_equal(al, e_al), "accept_len"
+    assert np.array_equal(bo, e_bo), "bonus"
+    assert np.array_equal(be, e_be), "best_node"
+    assert np.array_equal(rows, e_rows), "row_argmax"
+    return al
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [7, 2049, 20011, 151936])
+def test_tree_early_exit_random(dtype, V):
+    print(f"tree early-exit dtype={dtype} V={V}", flush=True)
+    Vd = min(V, 700)
+    al = _tree_case(B=6, N=61, V=V, Vd=Vd, dtype=dtype, seed=V + 5,
+                    children_max=min(10, Vd, V - 1))
+    assert al.min() >= 1
+
+
+def test_tree_early_exit_sizes_and_deep_paths():
+    print("tree early-exit sizes", flush=True)
+    for N in (1, 2, 5, 64, 65, 200, 1024):
+        _tree_case(B=3, N=N, V=2049, Vd=900, dtype="bf16", seed=N)
+    # path-shaped trees: ancestor masks span several 64-bit words
+    al = _tree_case(B=2, N=300, V=3001, Vd=1000, dtype="bf16", seed=7, p_match=1.0,
+                    depth_max=300, children_max=1)
+    assert (al == 300).all()
+    al = _tree_case(B=4, N=1024, V=2500, Vd=1000, dtype="bf16", seed=8, p_match=0.995,
+                    depth_max=1024, children_max=1)
+    assert al.max() > 64
+
+
+def test_tree_early_exit_malformed_and_duplicates():
+    print("tree early-exit malformed", flush=True)
+
+    def mutate(parent, ids, d2t):
+        parent[0, 5] = 7          # parent after the node
+        parent[1, 3] = -4         # negative parent
+        parent[2, 9] = 9          # self loop
+        ids[3, 1:6] = -1          # ids outside the draft vocabulary
+        ids[4, 1:6] = 10 ** 6
+        d2t[:50] = -7             # table entries outside the target vocabulary
+        d2t[50:100] = 10 ** 7
+        kids = np.flatnonzero(parent[5] == 0)
+        if len(kids) >= 2:
+            ids[5, kids[1]] = ids[5, kids[0]]   # two siblings with the same token
+    _tree_case(B=6, N=61, V=4099, Vd=600, dtype="bf16", seed=31, mutate=mutate)
+
+
+def test_tree_early_exit_workspace_reuse():
+    print("tree early-exit reuse", flush=True)
+    B, N, V = 16, 61, 20000
+    ws = torch.empty(wf.tree_early_exit_workspace_bytes(B, N, V), dtype=torch.uint8,
+                     device="cuda:0")
+    for seed, p in ((51, 0.0), (52, 1.0), (53, 0.7)):
+        _tree_case(B=B, N=N, V=V, Vd=900, dtype="bf16", seed=seed, ws=ws, p_match=p)
+
+
+def _routed_expect(t, offsets, choice, K, chain_draft, N, parent, ids, d2t, V):
+    al, bo, be = oracle.verify_routed(t, offsets, choice, K, chain_draft, N, parent, ids, d2t, V)
+    rows = np.full(t.shape[0], -1, np.int64)
+    for b in range(len(choice)):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if choice[b] == 0 and hi - lo == K + 1 and al[b] >= 1:
+            rows[lo:lo + al[b]] = t[lo:lo + al[b]]
+        elif choice[b] == 1 and hi - lo == N and al[b] >= 1:
+            acc, _ = oracle.tree_accepted(t[lo:hi], parent[b], ids[b], d2t, V)
+            rows[lo:hi] = np.where(acc, t[lo:hi], -1)
+    return al, bo, be, rows
+
+
+def _routed_case(layout, V, dtype, seed, mutate=None):
+    rb = make_routed_batch(seed, np.asarray(layout, np.int32), K=16, N=61, V=V, Vd=700, dtype=dtype)
+    offsets, choice = rb.offsets.copy(), rb.layout_choice.copy()
+    if mutate:
+        mutate(offsets, choice)
+    out = wf.verify_routed_early_exit(padded_logits(rb.logits, _stride(V)), dev(offsets), rb.rows,
+                                      dev(choice), dev(rb.chain_draft), dev(rb.parent),
+                                      dev(rb.draft_ids), dev(rb.d2t))
+    torch.cuda.synchronize()
+    al, bo, be, rows = (host(x) for x in out)
+    t = oracle.row_argmax(rb.logits, dtype)
+    e = _routed_expect(t, offsets, choice, 16, rb.chain_draft, 61, rb.parent, rb.draft_ids, rb.d2t,
+                       V)
+    assert np.array_equal(al, e[0]) and np.array_equal(bo, e[1]) and np.array_equal(be, e[2])
+    assert np.array_equal(rows, e[3]), "row_argmax"
+    return al
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_routed_early_exit_mixed(dtype):
+    print(f"routed early-exit dtype={dtype}", flush=True)
+    al = _routed_case([0, 1, 1, 0, 0, 1, 0, 1, 1, 1, 0, 0], 3001, dtype, seed=41)
+    assert al.min() >= 1
+
+
+def test_routed_early_exit_malformed():
+    print("routed early-exit malformed", flush=True)
+
+    def mutate(offsets, choice):
+        choice[1] = 1 - choice[1]   # row count no longer matches the choice
+        choice[2] = 5               # not a drafter
+    al = _routed_case([0, 1, 0, 1, 0, 1, 0, 1], 2500, "bf16", seed=42, mutate=mutate)
+    assert al[1] == 0 and al[2] == 0 and al[0] >= 1 and al[7] >= 1
+
+
+def test_routed_early_exit_workload_and_fused_round():
+    """The 128-sequence routed workload at full size: verify_routed_early_exit with the
+    oracle's routing choices, and round_routed_early_exit against route + the oracle."""
+    print("routed early-exit workload", flush=True)
+    batch, r = make_config(3)
+    t = oracle.row_argmax(batch.logits, "bf16")
+    logits = dev(batch.logits)
+    offs = dev(batch.offsets)
+    args = (dev(batch.chain_draft), dev(batch.parent), dev(batch.draft_ids), dev(batch.d2t))
+    e_dal, e_ch = oracle.route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)
+    e = _routed_expect(t, batch.offsets, e_ch, batch.K, batch.chain_draft, batch.N, batch.parent,
+                       batch.draft_ids, batch.d2t, batch.V)
+    runs = []
+    for _ in range(2):
+        out = wf.verify_routed_early_exit(logits, offs, batch.rows, dev(e_ch), *args)
+        runs.append([host(x) for x in out])
+    assert all(np.array_equal(a, b) for a, b in zip(*runs))
+    for got, want in zip(runs[0], e):
+        assert np.array_equal(got, want)
+    # fused round: router + early-exit verification with the router's own choice
+    b2 = torch.tensor([float(r.b2)], dtype=torch.float32, device="cuda:0")
+    dal, ch, al, bo, be, rows = wf.round_routed_early_exit(
+        dev(r.hidden), dev(r.W1), dev(r.b1), dev(r.W2), b2, r.tau, logits, offs, batch.rows, *args)
+    torch.cuda.synchronize()
+    check_router(host(dal), host(ch), e_dal, e_ch, r.dtype, r.tau)
+    far = np.abs(e_dal - r.tau) >= 1e-3
+    assert far.all(), "the workload keeps every gain away from the threshold"
+    for got, want in zip((al, bo, be, rows), e):
+        assert np.array_equal(host(got), want)

@@ -191,3 +191,66 @@ def test_routed_dispatch_and_malformed():
     over = np.array([0, 3, 6, 9, 15], np.int32)    # past total_rows
     al, _, _ = verify_routed(t_rows, over, choice, K, chain_draft, N, parent, ids, d2t, V)
     assert al[3] == MALFORMED_AL and al[0] == 3
+
+
+# ------------------------------------------------------------------ accepted-node sets
+
+
+def _accepted_by_path(t, parent, ids, d2t, V, u):
+    """Node u is accepted iff every edge on its walk up to the root is well formed and matches."""
+    while u != 0:
+        p = int(parent[u])
+        if not (0 <= p < u):
+            return False
+        did = int(ids[u])
+        if not (0 <= did < len(d2t)) or not (0 <= int(d2t[did]) < V) or int(d2t[did]) != int(t[p]):
+            return False
+        u = p
+    return True
+
+
+def test_tree_accepted_matches_root_path_walk():
+    from oracle import tree_accepted
+    rng = np.random.default_rng(21)
+    V, Vd = 4, 5
+    d2t = np.array([0, 1, 2, 3, 7], np.int32)      # id 4 maps outside the target vocabulary
+    for _ in range(2000):
+        N = int(rng.integers(1, 12))
+        parent = np.array([-1] + [int(rng.integers(-1, u + 1)) for u in range(1, N)], np.int32)
+        ids = rng.integers(-1, Vd + 1, size=N).astype(np.int32)
+        t = rng.integers(0, V, size=N).astype(np.int32)
+        acc, depth = tree_accepted(t, parent, ids, d2t, V)
+        for u in range(N):
+            assert acc[u] == _accepted_by_path(t, parent, ids, d2t, V, u)
+        al, bo, be = verify_tree(t[None], parent[None], ids[None], d2t, V)
+        assert acc[be[0]] and depth[be[0]] == al[0] - 1 == depth[acc].max()
+
+
+def test_tree_accepted_duplicate_siblings_both_accepted():
+    from oracle import tree_accepted
+    V = 6
+    d2t = np.arange(V, dtype=np.int32)
+    parent = np.array([-1, 0, 0, 1, 2], np.int32)
+    ids = np.array([-1, 3, 3, 5, 5], np.int32)     # siblings 1 and 2 carry the same token
+    t = np.array([3, 5, 5, 0, 0], np.int32)
+    acc, depth = tree_accepted(t, parent, ids, d2t, V)
+    assert acc.tolist() == [True, True, True, True, True]
+    assert depth.tolist() == [0, 1, 1, 2, 2]
+    al, bo, be = verify_tree(t[None], parent[None], ids[None], d2t, V)
+    assert (al[0], be[0]) == (3, 3)                # deepest, lowest index among equals
+
+
+def test_tree_accepted_of_a_chain_is_its_accepted_prefix():
+    from oracle import tree_accepted
+    rng = np.random.default_rng(22)
+    V = 5
+    d2t = np.arange(V, dtype=np.int32)
+    for _ in range(300):
+        K = int(rng.integers(0, 10))
+        t = rng.integers(0, V, size=K + 1).astype(np.int32)
+        draft = np.where(rng.random(K) < 0.7, t[:K], rng.integers(0, V, size=K)).astype(np.int32)
+        parent = np.arange(-1, K, dtype=np.int32)
+        ids = np.concatenate([[-1], draft]).astype(np.int32)
+        acc, _ = tree_accepted(t, parent, ids, d2t, V)
+        al, _ = verify_chain(t[None], draft[None])
+        assert acc.tolist() == [i < al[0] for i in range(K + 1)]

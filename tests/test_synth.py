@@ -86,3 +86,12 @@ def test_routed_layout_from_calibration():
 def test_make_config_structure_only():
     batch, router = make_config(3, logits=False)
     assert batch.rows == 64 * 17 + 64 * 61 and router.B == 128
+
+
+def test_tree_generator_rejects_more_children_than_draft_ids():
+    import pytest
+    from synth import make_tree_batch
+    with pytest.raises(ValueError):
+        make_tree_batch(1, 1, 20, V=7, Vd=7, children_max=10, logits=False)
+    with pytest.raises(ValueError):
+        make_tree_batch(1, 1, 20, V=7, Vd=7, children_max=7, logits=False)
