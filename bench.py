@@ -46,10 +46,13 @@ def _parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", choices=["routed", "sweep"], default="routed")
     p.add_argument("--pool", type=int, default=4, help="distinct rounds resident in HBM (sweep workload; routed early-exit)")
-    p.add_argument("--mode", choices=["fused", "separate", "early-exit"], default="fused",
+    p.add_argument("--mode", choices=["fused", "separate", "early-exit", "entropy",
+                                      "entropy-separate"], default="fused",
                    help="routed workload: whiflash_round_routed, whiflash_route then "
                         "whiflash_verify_routed, or whiflash_round_routed_early_exit over a pool "
-                        "of --pool rounds; sweep workload: early-exit verifies with "
+                        "of --pool rounds; entropy: the WhiFlash-Entropy round "
+                        "whiflash_verify_routed_entropy (entropy-separate: whiflash_verify_routed "
+                        "then whiflash_route_entropy); sweep workload: early-exit verifies with "
                         "whiflash_verify_chain_early_exit (rows up to the first mismatch only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -136,6 +139,13 @@ class Routed:
                                dtype=torch.uint8, device=dev)
         self.efws = torch.empty(wf.round_early_exit_workspace_bytes(B, r.m, K, N, self.rows, self.V),
                                 dtype=torch.uint8, device=dev)
+        self.layout = T(batch.layout_choice)
+        self.ent = torch.empty(B, dtype=torch.float32, device=dev)
+        self.nxt = torch.empty(B, dtype=torch.int32, device=dev)
+        self.entws = torch.empty(wf.verify_routed_entropy_workspace_bytes(B, self.rows, self.V),
+                                 dtype=torch.uint8, device=dev)
+        self.erws = torch.empty(wf.entropy_workspace_bytes(B, self.V), dtype=torch.uint8,
+                                device=dev)
         self.early = False
         self.wf = wf
         self.setup_s = time.time() - t0
@@ -168,6 +178,32 @@ class Routed:
         fn(p["logits"], self.offsets, self.rows, self.choice, p["chain_draft"], p["parent"],
            p["draft_ids"], self.d2t, row_argmax=False, accept_len=self.al, bonus=self.bonus,
            best_node=self.best, workspace=self.ews if self.early else self.vws)
+
+    # Entropy-policy threshold (nats): any fixed value; the decision is not fed back.
+    TAU_ENTROPY = 6.0
+
+    def entropy_step(self, i):
+        """One WhiFlash-Entropy round: verify with this round's choices, and the entropy at each
+        accepted row deciding the next round's drafter (one call)."""
+        p = self.pool[i % len(self.pool)]
+        self.wf.verify_routed_entropy(p["logits"], self.offsets, self.rows, self.layout, p["chain_draft"],
+                                      p["parent"], p["draft_ids"], self.d2t, self.TAU_ENTROPY,
+                                      row_argmax=False, accept_len=self.al, bonus=self.bonus,
+                                      best_node=self.best, entropy=self.ent, next_choice=self.nxt,
+                                      workspace=self.entws)
+
+    def entropy_separate_step(self, i):
+        p = self.pool[i % len(self.pool)]
+        self.wf.verify_routed(p["logits"], self.offsets, self.rows, self.layout, p["chain_draft"],
+                              p["parent"], p["draft_ids"], self.d2t, row_argmax=False,
+                              accept_len=self.al, bonus=self.bonus, best_node=self.best,
+                              workspace=self.vws)
+        self.entropy_only(i)
+
+    def entropy_only(self, i):
+        p = self.pool[i % len(self.pool)]
+        self.wf.route_entropy(p["logits"], self.best, self.TAU_ENTROPY, row0=self.offsets,
+                              entropy=self.ent, choice=self.nxt, workspace=self.erws)
 
     def fused_step(self, i):
         r = self.router
@@ -328,13 +364,23 @@ def main():
           file=sys.stderr, flush=True)
 
     early = args.mode == "early-exit"
+    entropy = args.mode in ("entropy", "entropy-separate")
+    if entropy and not hasattr(work, "entropy_step"):
+        print("--mode entropy applies to the routed workload", file=sys.stderr)
+        sys.exit(2)
     # The routed workload's early-exit step is the fused round; the chain workload has none.
     fused = args.mode in ("fused", "early-exit") and hasattr(work, "fused_step")
     if early:
         work.use_early_exit()
+    if entropy:
+        # This round's drafter choices are the layout's; the entropy decides the next round's.
+        work.choice.copy_(work.layout)
+        entropy_step = work.entropy_step if args.mode == "entropy" else work.entropy_separate_step
 
     def step(i):
-        if fused:
+        if entropy:
+            entropy_step(i)
+        elif fused:
             work.fused_step(i)
         else:
             work.route(i)
@@ -370,8 +416,13 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n / 1000.0
 
-    verify_s = timed_loop(work.verify, K)
-    route_s = timed_loop(work.route, K)
+    if entropy:
+        # The whole entropy round is the verify call; "route" is the separate entropy pass.
+        verify_s = timed_loop(entropy_step, K)
+        route_s = timed_loop(work.entropy_only, K)
+    else:
+        verify_s = timed_loop(work.verify, K)
+        route_s = timed_loop(work.route, K)
 
     ms_per_step = gpu_total_ms / K
     rounds_per_s = 1000.0 / ms_per_step
@@ -380,7 +431,9 @@ def main():
     alg_bytes = work.needed_bytes if early else work.logits_bytes
     achieved = alg_bytes / verify_s / 1e9
     traffic = None if early else _traffic(work.name, work.logits_bytes)
-    mode = ("whiflash_round_routed_early_exit" if fused and early else
+    mode = ("whiflash_verify_routed_entropy" if args.mode == "entropy" else
+            "whiflash_verify_routed + whiflash_route_entropy" if args.mode == "entropy-separate" else
+            "whiflash_round_routed_early_exit" if fused and early else
             "whiflash_round_routed" if fused else
             "whiflash_route + whiflash_verify_chain_early_exit" if early else
             "whiflash_route + whiflash_verify_*")

@@ -18,6 +18,9 @@ Entry points (same names as the C ABI):
     verify_routed(logits, row_offsets, total_rows, choice, chain_draft, parent, draft_ids, d2t)
                                                           -> (accept_len, bonus, best_node, row_argmax)
     route_entropy(logits, pos, tau, row0=None, rows_per_seq=0)  -> (entropy, choice)
+    verify_routed_entropy(logits, row_offsets, total_rows, choice, chain_draft, parent, draft_ids,
+                          d2t, tau)   verify_routed + the entropy policy at the accepted rows
+                          -> (accept_len, bonus, best_node, row_argmax, entropy, next_choice)
     catchup_update(cur_choice, accept_len, next_choice, backlog)  -> (switch_flag, catchup_len)
     round_routed(hidden, W1, b1, W2, b2, tau, logits, row_offsets, total_rows, chain_draft,
                  parent, draft_ids, d2t)   route + verify_routed fused
@@ -53,6 +56,9 @@ from ._binding import (  # noqa: F401
     whiflash_verify_chain_early_exit,
     verify_routed,
     route_entropy,
+    verify_routed_entropy,
+    verify_routed_entropy_workspace_bytes,
+    whiflash_verify_routed_entropy,
     entropy_workspace_bytes,
     catchup_update,
     whiflash_catchup_update,

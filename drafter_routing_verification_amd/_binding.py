@@ -48,6 +48,11 @@ _SIGNATURES = {
                                                   _c_i64, _c_p, _c_i32, _c_i32, _c_p, _c_i32, _c_p,
                                                   _c_p, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p,
                                                   _c_sz, _c_p]),
+    "whiflash_verify_routed_entropy_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32]),
+    "whiflash_verify_routed_entropy": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_i32,
+                                                _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_i32,
+                                                _c_f, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                _c_sz, _c_p]),
     "whiflash_verify_tree": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
                                       _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_route_gather": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p,
@@ -143,6 +148,14 @@ def routed_early_exit_workspace_bytes(B: int, K: int, N: int, total_rows: int, V
 
 def round_early_exit_workspace_bytes(B: int, m: int, K: int, N: int, total_rows: int, V: int) -> int:
     return int(lib().whiflash_round_early_exit_workspace_bytes(B, m, K, N, total_rows, V))
+
+
+def whiflash_verify_routed_entropy(*args):
+    return lib().whiflash_verify_routed_entropy(*args)
+
+
+def verify_routed_entropy_workspace_bytes(B: int, total_rows: int, V: int) -> int:
+    return int(lib().whiflash_verify_routed_entropy_workspace_bytes(B, total_rows, V))
 
 
 def whiflash_verify_tree(*args):
@@ -556,3 +569,43 @@ def round_routed_early_exit(hidden, W1, b1, W2, b2, tau: float, logits, row_offs
     """round_routed with the early-exit verification (four launches)."""
     return round_routed(hidden, W1, b1, W2, b2, tau, logits, row_offsets, total_rows, chain_draft,
                         parent, draft_ids, d2t, _early=True, **kw)
+
+
+def verify_routed_entropy(logits, row_offsets, total_rows: int, choice, chain_draft, parent,
+                          draft_ids, d2t, tau: float, *, row_argmax=True, accept_len=None,
+                          bonus=None, best_node=None, entropy=None, next_choice=None,
+                          workspace=None, stream=None):
+    """verify_routed plus the entropy policy at each accepted row (one call).
+    Returns (accept_len, bonus, best_node, row_argmax, entropy, next_choice)."""
+    _device_tensor(choice, "choice")
+    B = choice.numel()
+    if logits.dim() != 2:
+        raise ValueError("routed logits must be [total_rows, V]")
+    V, stride = _rows_view(logits, total_rows)
+    _i32(row_offsets, "row_offsets", B + 1)
+    _i32(choice, "choice", B)
+    K = chain_draft.shape[1]
+    N = parent.shape[1]
+    _i32(chain_draft, "chain_draft", B * K)
+    _i32(parent, "parent", B * N)
+    _i32(draft_ids, "draft_ids", B * N)
+    _i32(d2t, "d2t")
+    dev = logits.device
+    new = lambda dt: torch.empty(B, dtype=dt, device=dev)
+    accept_len = new(torch.int32) if accept_len is None else accept_len
+    bonus = new(torch.int32) if bonus is None else bonus
+    best_node = new(torch.int32) if best_node is None else best_node
+    entropy = new(torch.float32) if entropy is None else entropy
+    next_choice = new(torch.int32) if next_choice is None else next_choice
+    if row_argmax is True:
+        row_argmax = torch.empty(max(total_rows, 1), dtype=torch.int32, device=dev)
+    elif row_argmax is False:
+        row_argmax = None
+    ws = _workspace(workspace, verify_routed_entropy_workspace_bytes(B, total_rows, V), dev)
+    _check(whiflash_verify_routed_entropy(
+        _ptr(logits), _dtype_code(logits), B, V, stride, _ptr(row_offsets), total_rows,
+        _ptr(choice), K, _ptr(chain_draft), N, _ptr(parent), _ptr(draft_ids), _ptr(d2t),
+        d2t.numel(), float(tau), _ptr(accept_len), _ptr(bonus), _ptr(best_node), _ptr(row_argmax),
+        _ptr(entropy), _ptr(next_choice), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(logits, stream)))
+    return accept_len, bonus, best_node, row_argmax, entropy, next_choice

@@ -482,4 +482,55 @@ int32_t whiflash_round_routed_early_exit(
                       hidden_dtype, zp, m, b1, W2, b2, tau, delta_al, choice);
 }
 
+size_t whiflash_verify_routed_entropy_workspace_bytes(int32_t B, int32_t total_rows, int32_t V) {
+  if (B <= 0 || total_rows <= 0 || V <= 0) return 0;
+  // Chunk partials of the sweep, the best nodes when the caller passes none,
+  // then the entropy pass's partials.
+  return whiflash_verify_workspace_bytes(total_rows, V) +
+         round_up(static_cast<size_t>(B) * sizeof(int32_t), kWorkspaceAlign) +
+         whiflash_entropy_workspace_bytes(B, V);
+}
+
+int32_t whiflash_verify_routed_entropy(const void* logits, int32_t dtype, int32_t B, int32_t V,
+                                       int64_t row_stride, const int32_t* row_offsets,
+                                       int32_t total_rows, const int32_t* choice, int32_t K,
+                                       const int32_t* chain_draft, int32_t N,
+                                       const int32_t* parent, const int32_t* draft_ids,
+                                       const int32_t* d2t, int32_t Vd, float tau_entropy,
+                                       int32_t* accept_len, int32_t* bonus, int32_t* best_node,
+                                       int32_t* row_argmax, float* entropy, int32_t* next_choice,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  if (B < 0 || total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+      N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
+    return WF_ERR_SHAPE;
+  int32_t s = check_logits(logits, dtype, total_rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (B > INT32_MAX / 64) return WF_ERR_SHAPE;
+  if (!row_offsets || !choice || (K > 0 && !chain_draft) || !parent || !draft_ids || !d2t ||
+      !accept_len || !bonus || !entropy || !next_choice)
+    return WF_ERR_NULL;
+  if ((s = check_workspace(workspace, workspace_bytes,
+                           whiflash_verify_routed_entropy_workspace_bytes(B, total_rows, V))) !=
+      WF_OK)
+    return s;
+  char* ws = static_cast<char*>(workspace);
+  const size_t part_bytes = whiflash_verify_workspace_bytes(total_rows, V);
+  const size_t best_bytes = round_up(static_cast<size_t>(B) * sizeof(int32_t), kWorkspaceAlign);
+  const wf::SweepPlan plan = wf::sweep_plan(total_rows, V);
+  wf::Partial* part = reinterpret_cast<wf::Partial*>(ws);
+  int32_t* best = best_node ? best_node : reinterpret_cast<int32_t*>(ws + part_bytes);
+  if (wf::launch_sweep(logits, dtype, row_stride, total_rows, V, plan, part, stream) != hipSuccess)
+    return WF_ERR_LAUNCH;
+  if (wf::launch_finalize_routed(false, part, plan.splits, B, V, row_offsets, total_rows, choice, K,
+                                 chain_draft, N, parent, draft_ids, d2t, Vd, accept_len, bonus,
+                                 best, row_argmax, stream) != hipSuccess)
+    return WF_ERR_LAUNCH;
+  // Malformed sequences have best node -1, which selects no row: H = NaN, choice 0.
+  return launch_status(wf::launch_entropy(logits, dtype, row_stride, total_rows, V, B, row_offsets,
+                                          0, best, tau_entropy, entropy, next_choice,
+                                          ws + part_bytes + best_bytes, stream));
+}
+
 }  // extern "C"

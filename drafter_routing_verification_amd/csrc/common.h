@@ -55,6 +55,7 @@ __device__ inline int64_t hidden_row(const HiddenSel& s, int b) {
 hipError_t launch_sweep(const void* logits, int dtype, int64_t row_stride, int32_t rows, int32_t V,
                         SweepPlan plan, Partial* part, hipStream_t stream);
 
+
 // Early-exit verification of trees and routed batches (see early_exit.hip).
 constexpr int kMaxMaskWords = (kMaxSeqRows + 63) / 64;
 

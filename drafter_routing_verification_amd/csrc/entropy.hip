@@ -12,36 +12,12 @@
 
 #include "common.h"
 #include "elem.h"
+#include "ent_math.h"
 
 namespace wf {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kEntUnroll = 4;
-
-struct Ent {
-  float m, S, U;
-};
-
-// Folds (m2, S2, U2) into (m, S, U).
-__device__ inline void ent_merge(Ent& a, const Ent& b) {
-  if (b.S == 0.f) return;
-  if (a.S == 0.f) {
-    a = b;
-    return;
-  }
-  const float M = fmaxf(a.m, b.m);
-  const float da = (a.m - M) * kLog2e, db = (b.m - M) * kLog2e;
-  const float fa = __builtin_amdgcn_exp2f(da), fb = __builtin_amdgcn_exp2f(db);
-  a.U = (a.U + da * a.S) * fa + (b.U + db * b.S) * fb;
-  a.S = a.S * fa + b.S * fb;
-  a.m = M;
-}
-
-__device__ inline Ent shfl_xor(const Ent& e, int off) {
-  return Ent{__shfl_xor(e.m, off), __shfl_xor(e.S, off), __shfl_xor(e.U, off)};
-}
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void entropy_partial_kernel(
@@ -62,23 +38,10 @@ __global__ __launch_bounds__(kThreads) void entropy_partial_kernel(
     const int v1 = min(v0 + chunk_vecs, nvec);
     auto absorb = [&](u32x4 d) {
       const float mv = E::vmax(d);
-      if (mv > acc.m) {
-        if (acc.S != 0.f) {
-          const float dl = (acc.m - mv) * kLog2e;
-          const float f = __builtin_amdgcn_exp2f(dl);
-          acc.U = (acc.U + dl * acc.S) * f;
-          acc.S *= f;
-        }
-        acc.m = mv;
-      }
+      if (mv > acc.m) ent_raise(acc, mv);
       const float mb = acc.m * kLog2e;
 #pragma unroll
-      for (int k = 0; k < E::kPerVec; ++k) {
-        const float y = fmaf(E::at(d, k), kLog2e, -mb);
-        const float e = __builtin_amdgcn_exp2f(y);
-        acc.S += e;
-        acc.U = fmaf(y, e, acc.U);
-      }
+      for (int k = 0; k < E::kPerVec; ++k) ent_add(acc, E::at(d, k), mb);
     };
     int v = v0 + tid;
     for (; v + (kEntUnroll - 1) * kThreads < v1; v += kEntUnroll * kThreads) {
@@ -99,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void entropy_partial_kernel(
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const Ent o = shfl_xor(acc, off);
+    const Ent o = ent_shfl_xor(acc, off);
     ent_merge(acc, o);
   }
   __shared__ Ent red[kWaves];
@@ -127,12 +90,12 @@ __global__ __launch_bounds__(kThreads) void entropy_finish_kernel(
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const Ent o = shfl_xor(acc, off);
+    const Ent o = ent_shfl_xor(acc, off);
     ent_merge(acc, o);
   }
   if (lane == 0) {
     const bool valid = select_row(row0, rows_per_seq, pos, total_rows, b) >= 0 && acc.S > 0.f;
-    const float H = valid ? kLn2 * (__builtin_amdgcn_logf(acc.S) - acc.U / acc.S) : NAN;
+    const float H = valid ? ent_value(acc) : NAN;
     entropy[b] = H;
     choice[b] = (valid && H > tau) ? 1 : 0;
   }

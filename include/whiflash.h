@@ -359,6 +359,36 @@ int32_t whiflash_round_routed_early_exit(
     int32_t* accept_len, int32_t* bonus, int32_t* best_node, int32_t* row_argmax, void* workspace,
     size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes of whiflash_verify_routed_entropy (host-only; 0 on bad sizes). */
+size_t whiflash_verify_routed_entropy_workspace_bytes(int32_t B, int32_t total_rows, int32_t V);
+
+/*
+ * One round of the WhiFlash-Entropy policy (WhiFlash paper, section 3.3.1:
+ * the entropy of the target's next-token distribution at the final accepted
+ * position decides the next drafter): whiflash_verify_routed, then the entropy
+ * of the softmax of each sequence's accepted row (its first row + best node)
+ * and its threshold, as whiflash_route_entropy computes them.  Arguments,
+ * layouts and errors are those of whiflash_verify_routed plus:
+ *   tau_entropy  threshold on H (nats);
+ *   entropy [B] float32  H of the accepted row (NaN for malformed sequences);
+ *   next_choice [B] int32  1 (EAGLE-3) iff H > tau_entropy, else 0.
+ * best_node may be NULL (the workspace then holds it).  Results equal those
+ * of whiflash_verify_routed followed by whiflash_route_entropy(row0 =
+ * row_offsets, pos = best_node).  Finite logits are required for H.
+ * Workspace: whiflash_verify_routed_entropy_workspace_bytes(B, total_rows, V)
+ * bytes, 256-byte aligned.
+ */
+int32_t whiflash_verify_routed_entropy(const void* logits, int32_t dtype, int32_t B, int32_t V,
+                                       int64_t row_stride, const int32_t* row_offsets,
+                                       int32_t total_rows, const int32_t* choice, int32_t K,
+                                       const int32_t* chain_draft, int32_t N,
+                                       const int32_t* parent, const int32_t* draft_ids,
+                                       const int32_t* d2t, int32_t Vd, float tau_entropy,
+                                       int32_t* accept_len, int32_t* bonus, int32_t* best_node,
+                                       int32_t* row_argmax, float* entropy, int32_t* next_choice,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

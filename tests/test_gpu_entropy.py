@@ -97,3 +97,54 @@ def test_entropy_at_accepted_rows_of_routed_workload():
     H, ch = wf.route_entropy(logits, be, tau, row0=offs)
     H_ref, ch_ref = oracle.route_entropy(batch.logits, "bf16", rows, tau)
     _check(host(H), host(ch), H_ref, ch_ref, tau)
+
+
+def _routed_entropy_case(batch, logits_dev, tau_from_median=True, mutate=None):
+    offsets, choice = batch.offsets.copy(), batch.layout_choice.copy()
+    if mutate:
+        mutate(offsets, choice)
+    t = oracle.row_argmax(batch.logits, batch.dtype)
+    e_al, e_bo, e_be = oracle.verify_routed(t, offsets, choice, batch.K, batch.chain_draft,
+                                            batch.N, batch.parent, batch.draft_ids, batch.d2t,
+                                            batch.V)
+    rows = np.where(e_be >= 0, offsets[:-1] + e_be, -1)
+    ok_rows = rows[rows >= 0]
+    tau = float(np.median([oracle.entropy(batch.logits[r], batch.dtype) for r in ok_rows[:9]]))
+    out = wf.verify_routed_entropy(logits_dev, dev(offsets), batch.rows, dev(choice),
+                                   dev(batch.chain_draft), dev(batch.parent), dev(batch.draft_ids),
+                                   dev(batch.d2t), tau)
+    torch.cuda.synchronize()
+    al, bo, be, rr, H, nxt = (host(x) for x in out)
+    assert np.array_equal(al, e_al) and np.array_equal(bo, e_bo) and np.array_equal(be, e_be)
+    covered = np.zeros(batch.rows, bool)
+    for b in range(len(choice)):
+        if 0 <= offsets[b] <= offsets[b + 1] <= batch.rows:
+            covered[offsets[b]:offsets[b + 1]] = True
+    assert np.array_equal(rr[covered], t[covered])
+    H_ref, ch_ref = oracle.route_entropy(batch.logits, batch.dtype, rows, tau)
+    _check(H, nxt, H_ref, ch_ref, tau)
+    return H, nxt
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_verify_routed_entropy_small(dtype):
+    """Fused verify + entropy policy on a ragged mix with ragged vocabulary, and malformed
+    sequences (entropy NaN, next choice 0)."""
+    from synth import make_routed_batch
+    print(f"verify_routed_entropy dtype={dtype}", flush=True)
+    V = 3001
+    rb = make_routed_batch(61, np.array([0, 1, 1, 0, 0, 1, 0, 1, 1, 0], np.int32), K=16, N=61,
+                           V=V, Vd=700, dtype=dtype)
+    logits = padded_logits(rb.logits, (V + 7) // 8 * 8 + 8)
+
+    def mutate(offsets, choice):
+        choice[3] = 1          # row count no longer matches the choice
+    H, nxt = _routed_entropy_case(rb, logits, mutate=mutate)
+    assert np.isnan(H[3]) and nxt[3] == 0 and not np.isnan(H[0])
+
+
+def test_verify_routed_entropy_workload():
+    """The 128-sequence routed workload at full size."""
+    print("verify_routed_entropy on routed_bf16", flush=True)
+    batch, _ = make_config(3)
+    _routed_entropy_case(batch, dev(batch.logits))
