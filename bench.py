@@ -416,6 +416,21 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n / 1000.0
 
+    def step_distribution(fn, n):
+        """Per-step durations (HIP events around each step, launched back to back)."""
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(n):
+            fn(i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1000.0 for i in range(n)])
+        return {"p10": round(float(np.percentile(us, 10)), 2),
+                "p50": round(float(np.percentile(us, 50)), 2),
+                "p90": round(float(np.percentile(us, 90)), 2), "steps": n}
+
+    step_us = step_distribution(step, min(K, 200))
     if entropy:
         # The whole entropy round is the verify call; "route" is the separate entropy pass.
         verify_s = timed_loop(entropy_step, K)
@@ -458,6 +473,7 @@ def main():
         "route_us": round(route_s * 1e6, 2),
         "verify_us": round(verify_s * 1e6, 2),
         "wall_ms_per_step": round(wall * 1000 / K, 5),
+        "step_us": step_us,
         "mean_accept_len": round(mean_al, 3),
         **({"logits_bytes_needed_per_round": round(alg_bytes)} if early else {}),
         "roofline": {
