@@ -101,7 +101,7 @@ class Routed:
         from synth.workloads import CONFIGS, PLANT_BOOST
         import drafter_routing_verification_amd as wf
         t0 = time.time()
-        batch, r = make_config(3)
+        batch, r = make_config("routed_bf16")
         self.batch, self.router = batch, r
         self.V, self.rows, self.B = batch.V, batch.rows, batch.B
         T = lambda a: _to_dev(a, torch, dev)
@@ -111,7 +111,7 @@ class Routed:
         self.offsets, self.d2t = T(batch.offsets), T(batch.d2t)
         self.pool = [dict(logits=T(batch.logits), chain_draft=T(batch.chain_draft),
                           parent=T(batch.parent), draft_ids=T(batch.draft_ids))]
-        c = CONFIGS[3]
+        c = CONFIGS["routed_bf16"]
         g = torch.Generator(device=dev)
         for rnd in range(1, pool):
             rb = make_routed_batch(c["seed"], batch.layout_choice, c["K"], c["N"], self.V,
@@ -251,7 +251,7 @@ class Sweep:
         from synth.workloads import CONFIGS, V_QWEN3, PLANT_BOOST
         import drafter_routing_verification_amd as wf
         t0 = time.time()
-        c = CONFIGS[4]
+        c = CONFIGS["sweep_bf16"]
         self.B, self.K, self.V = c["B"], c["K"], V_QWEN3
         self.rows = self.B * (self.K + 1)
         self.pool = []

@@ -309,19 +309,19 @@ def make_routed_batch(seed: int, layout_choice: np.ndarray, K: int = 16, N: int 
 
 # --------------------------------------------------------------------------- configs
 
+# The five workloads, by name (seeds 0-4).
 CONFIGS = {
-    0: dict(name="single_chain_f32", seed=0, kind="chain", B=1, K=16, dtype="f32", router=True),
-    1: dict(name="batched_chain_bf16", seed=1, kind="chain", B=32, K=16, dtype="bf16", router=True),
-    2: dict(name="tree_bf16", seed=2, kind="tree", B=8, N=61, dtype="bf16", router=False),
-    3: dict(name="routed_bf16", seed=3, kind="routed", B=128, K=16, N=61, dtype="bf16", router=True),
-    4: dict(name="sweep_bf16", seed=4, kind="chain", B=256, K=16, dtype="bf16", router=True,
-            rounds=100),
+    "single_chain_f32": dict(seed=0, kind="chain", B=1, K=16, dtype="f32", router=True),
+    "batched_chain_bf16": dict(seed=1, kind="chain", B=32, K=16, dtype="bf16", router=True),
+    "tree_bf16": dict(seed=2, kind="tree", B=8, N=61, dtype="bf16", router=False),
+    "routed_bf16": dict(seed=3, kind="routed", B=128, K=16, N=61, dtype="bf16", router=True),
+    "sweep_bf16": dict(seed=4, kind="chain", B=256, K=16, dtype="bf16", router=True, rounds=100),
 }
 
 
-def make_config(idx: int, rnd: int = 0, logits: bool = True, V: int = V_QWEN3):
+def make_config(name: str, rnd: int = 0, logits: bool = True, V: int = V_QWEN3):
     """Returns (batch, router_inputs_or_None) for one of the five workloads."""
-    c = CONFIGS[idx]
+    c = CONFIGS[name]
     seed = c["seed"]
     if c["kind"] == "chain":
         batch = make_chain_batch(seed, c["B"], c["K"], V, c["dtype"], 0.8, rnd, logits)

@@ -20,7 +20,7 @@ sys.path.insert(0, ROOT)
 from oracle import route                       # noqa: E402
 from synth.workloads import CONFIGS, TAU, make_router_inputs  # noqa: E402
 
-cfg = CONFIGS[3]
+cfg = CONFIGS["routed_bf16"]
 r = make_router_inputs(cfg["seed"], cfg["B"], dtype=cfg["dtype"], b2=0.0)
 dal0, _ = route(r.hidden, r.W1, r.b1, r.W2, 0.0, TAU, cfg["dtype"])
 s = np.sort(dal0)

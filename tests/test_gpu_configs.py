@@ -12,7 +12,6 @@ import drafter_routing_verification_amd as wf
 import oracle
 from gpu_helpers import check_router, dev, host
 from synth import make_config
-from synth.workloads import CONFIGS
 
 pytestmark = pytest.mark.gpu
 
@@ -27,9 +26,9 @@ def _route(r):
     return out1[1], e_ch
 
 
-def _chain(idx, rnd=0):
-    print(f"workload {CONFIGS[idx]['name']} round {rnd}", flush=True)
-    batch, router = make_config(idx, rnd=rnd)
+def _chain(name, rnd=0):
+    print(f"workload {name} round {rnd}", flush=True)
+    batch, router = make_config(name, rnd=rnd)
     _route(router)
     logits = dev(batch.logits)
     runs = [[host(x) for x in wf.verify_chain(logits, dev(batch.draft))] for _ in range(2)]
@@ -43,18 +42,18 @@ def _chain(idx, rnd=0):
 
 
 def test_single_chain_f32():
-    al = _chain(0)
+    al = _chain("single_chain_f32")
     assert 1 <= al[0] <= 17
 
 
 def test_batched_chain_bf16():
-    al = _chain(1)
+    al = _chain("batched_chain_bf16")
     assert 3.0 < al.mean() < 7.0
 
 
 def test_tree_bf16():
     print("workload tree_bf16", flush=True)
-    batch, _ = make_config(2)
+    batch, _ = make_config("tree_bf16")
     logits = dev(batch.logits)
     args = (logits, dev(batch.parent), dev(batch.draft_ids), dev(batch.d2t))
     runs = [[host(x) for x in wf.verify_tree(*args)] for _ in range(2)]
@@ -69,7 +68,7 @@ def test_tree_bf16():
 
 def test_routed_bf16():
     print("workload routed_bf16", flush=True)
-    batch, router = make_config(3)
+    batch, router = make_config("routed_bf16")
     ch_gpu, ch_ref = _route(router)
     assert np.array_equal(ch_ref, batch.layout_choice)
     # the device choice of the router drives the dispatch, as in the benchmark
@@ -91,7 +90,7 @@ def test_routed_bf16():
 
 @pytest.mark.parametrize("rnd", [0, 57])
 def test_sweep_bf16(rnd):
-    al = _chain(4, rnd)
+    al = _chain("sweep_bf16", rnd)
     assert 4.0 < al.mean() < 5.8
 
 

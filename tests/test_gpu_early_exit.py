@@ -14,7 +14,6 @@ import drafter_routing_verification_amd as wf
 import oracle
 from gpu_helpers import dev, host, padded_logits
 from synth import f32_to_bf16_bits, make_chain_batch, make_config
-from synth.workloads import CONFIGS
 
 pytestmark = pytest.mark.gpu
 
@@ -118,11 +117,11 @@ def test_early_exit_matches_full_verify_without_row_argmax():
     assert torch.equal(al, f_al) and torch.equal(bo, f_bo)
 
 
-@pytest.mark.parametrize("idx,rnd", [(1, 0), (4, 0), (4, 57)])
-def test_early_exit_workloads(idx, rnd):
+@pytest.mark.parametrize("name,rnd", [("batched_chain_bf16", 0), ("sweep_bf16", 0), ("sweep_bf16", 57)])
+def test_early_exit_workloads(name, rnd):
     """The batched chain workloads at full size, twice (results must not vary)."""
-    print(f"early-exit workload {CONFIGS[idx]['name']} round {rnd}", flush=True)
-    batch, _ = make_config(idx, rnd=rnd)
+    print(f"early-exit workload {name} round {rnd}", flush=True)
+    batch, _ = make_config(name, rnd=rnd)
     logits = dev(batch.logits)
     runs = [_run(logits, batch.draft) for _ in range(2)]
     assert all(np.array_equal(a, b) for a, b in zip(*runs))

@@ -155,7 +155,7 @@ def test_routed_early_exit_workload_and_fused_round():
     """The 128-sequence routed workload at full size: verify_routed_early_exit with the
     oracle's routing choices, and round_routed_early_exit against route + the oracle."""
     print("routed early-exit workload", flush=True)
-    batch, r = make_config(3)
+    batch, r = make_config("routed_bf16")
     t = oracle.row_argmax(batch.logits, "bf16")
     logits = dev(batch.logits)
     offs = dev(batch.offsets)

@@ -79,7 +79,7 @@ def test_entropy_rows(dtype, V):
 def test_entropy_at_accepted_rows_of_routed_workload():
     """Routed bf16 workload: verify, then the entropy policy at each sequence's accepted row."""
     print("entropy on routed_bf16", flush=True)
-    batch, _ = make_config(3)
+    batch, _ = make_config("routed_bf16")
     logits = dev(batch.logits)
     offs, choice = dev(batch.offsets), dev(batch.layout_choice)
     al, bo, be, _ = wf.verify_routed(logits, offs, batch.rows, choice, dev(batch.chain_draft),
@@ -146,5 +146,5 @@ def test_verify_routed_entropy_small(dtype):
 def test_verify_routed_entropy_workload():
     """The 128-sequence routed workload at full size."""
     print("verify_routed_entropy on routed_bf16", flush=True)
-    batch, _ = make_config(3)
+    batch, _ = make_config("routed_bf16")
     _routed_entropy_case(batch, dev(batch.logits))

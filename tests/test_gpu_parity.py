@@ -187,3 +187,29 @@ def test_router_deterministic():
     a = host(wf.route(*args)[0])
     b = host(wf.route(*args)[0])
     assert np.array_equal(a, b)
+
+
+def test_many_rows_small_vocab():
+    """Large batches (tens of thousands of rows) with a ragged vocabulary: grid and row
+    arithmetic of the full and early-exit paths at sizes far beyond the workloads'."""
+    print("many rows", flush=True)
+    V = 520                                   # 65 bf16 vectors per row
+    cb = make_chain_batch(71, 3000, 16, V, "bf16")
+    logits = padded_logits(cb.logits, _stride(V))
+    t = oracle.row_argmax(cb.logits, "bf16")
+    e_al, e_bo = oracle.verify_chain(t.reshape(3000, 17), cb.draft)
+    al, bo, rows = (host(x) for x in wf.verify_chain(logits, dev(cb.draft)))
+    assert np.array_equal(rows, t) and np.array_equal(al, e_al) and np.array_equal(bo, e_bo)
+    al, bo, _ = (host(x) for x in wf.verify_chain_early_exit(logits, dev(cb.draft)))
+    assert np.array_equal(al, e_al) and np.array_equal(bo, e_bo)
+    layout = np.arange(1200, dtype=np.int32) % 2
+    rb = make_routed_batch(72, layout, K=16, N=61, V=V, Vd=300, dtype="bf16")
+    logits = padded_logits(rb.logits, _stride(V))
+    t = oracle.row_argmax(rb.logits, "bf16")
+    e = oracle.verify_routed(t, rb.offsets, layout, 16, rb.chain_draft, 61, rb.parent,
+                             rb.draft_ids, rb.d2t, V)
+    args = (logits, dev(rb.offsets), rb.rows, dev(layout), dev(rb.chain_draft), dev(rb.parent),
+            dev(rb.draft_ids), dev(rb.d2t))
+    for fn in (wf.verify_routed, wf.verify_routed_early_exit):
+        al, bo, be, _ = (host(x) for x in fn(*args))
+        assert np.array_equal(al, e[0]) and np.array_equal(bo, e[1]) and np.array_equal(be, e[2])

@@ -64,7 +64,7 @@ def test_round_small(B, d, m):
 
 def test_round_routed_workload():
     print("round on routed_bf16", flush=True)
-    batch, r = make_config(3)
+    batch, r = make_config("routed_bf16")
     out = _run(r, batch, dev(batch.logits), r.b2)
     _oracle(r, batch, r.b2, out)
     assert np.array_equal(out[1], batch.layout_choice) and out[2].min() >= 1

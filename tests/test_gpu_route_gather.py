@@ -51,7 +51,7 @@ def test_route_gather_small(dtype, B, d, m):
 def test_route_gather_routed_workload():
     """Verify the routed batch, then route its next round from the accepted rows."""
     print("route_gather on routed_bf16", flush=True)
-    batch, r = make_config(3)
+    batch, r = make_config("routed_bf16")
     logits = dev(batch.logits)
     offs = dev(batch.offsets)
     _, _, be, _ = wf.verify_routed(logits, offs, batch.rows, dev(batch.layout_choice),

@@ -76,7 +76,7 @@ def test_router_inputs_scale():
 
 def test_routed_layout_from_calibration():
     cal = routed_calibration()
-    assert len(cal["choice"]) == CONFIGS[3]["B"] and sum(cal["choice"]) == 64
+    assert len(cal["choice"]) == CONFIGS["routed_bf16"]["B"] and sum(cal["choice"]) == 64
     rb = make_routed_batch(3, np.array(cal["choice"][:6]), V=1000, logits=True)
     rows = [61 if c else 17 for c in cal["choice"][:6]]
     assert np.array_equal(np.diff(rb.offsets), rows)
@@ -84,7 +84,7 @@ def test_routed_layout_from_calibration():
 
 
 def test_make_config_structure_only():
-    batch, router = make_config(3, logits=False)
+    batch, router = make_config("routed_bf16", logits=False)
     assert batch.rows == 64 * 17 + 64 * 61 and router.B == 128
 
 
