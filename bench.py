@@ -2,17 +2,19 @@
 
 One step = one speculation round over a batch: the neural router
 (whiflash_route) followed by greedy verification of that batch's candidates
-(whiflash_verify_routed: argmax sweep over every logits row, d2t remap,
-chain / tree acceptance, emission), on one HIP stream.
+(argmax sweep over every logits row, chain / tree acceptance, emission), on
+one HIP stream.
 
 Workloads:
-  routed (default): 128 sequences, bf16 hidden [128, 2560] through the router
+  sweep (default): the throughput sweep: 256 DFlash chains, K = 16, bf16 logits
+      [256, 17, 151936] (1.32 GB per round) plus the router on bf16 hidden
+      [256, 2560] (MFMA path); 100 rounds with fresh seeded logits, drafts and
+      hidden states each, all resident in HBM (132 GB) and cycled.
+  routed: 128 sequences, bf16 hidden [128, 2560] through the router
       (2560 -> 1024 -> 1, threshold 1.0, exact 64/64 split); 64 DFlash chains of
       K = 16 (17 rows) and 64 EAGLE-3 trees of 61 nodes, packed into 4,992 bf16
-      logits rows of 151,936 (1.517 GB per round).
-  sweep: 256 DFlash chains, K = 16, bf16 logits [256, 17, 151936] (1.32 GB per
-      round) plus the router on bf16 hidden [256, 2560]; a pool of distinct
-      seeded rounds resident in HBM is cycled so every step reads fresh logits.
+      logits rows of 151,936 (1.517 GB per round); one step is
+      whiflash_round_routed.
 
 Prints one JSON line (rounds/s, logits GB/s, roofline of the argmax sweep and
 the CPU oracle baseline).
@@ -44,8 +46,10 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", choices=["routed", "sweep"], default="routed")
-    p.add_argument("--pool", type=int, default=4, help="distinct rounds resident in HBM (sweep workload; routed early-exit)")
+    p.add_argument("--workload", choices=["sweep", "routed"], default="sweep")
+    p.add_argument("--pool", type=int, default=None,
+                   help="distinct rounds resident in HBM (default: 100 for the sweep workload, "
+                        "4 for the routed early-exit mode)")
     p.add_argument("--mode", choices=["fused", "separate", "early-exit", "entropy",
                                       "entropy-separate"], default="fused",
                    help="routed workload: whiflash_round_routed, whiflash_route then "
@@ -356,9 +360,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     if args.workload == "routed":
-        work = Routed(torch, dev, args.pool if args.mode == "early-exit" else 1)
+        work = Routed(torch, dev, (args.pool or 4) if args.mode == "early-exit" else 1)
     else:
-        work = Sweep(torch, dev, args.pool)
+        work = Sweep(torch, dev, args.pool or 100)
     stream = torch.cuda.current_stream()
     print(f"# workload {work.name}: inputs resident in HBM ({work.setup_s:.1f} s setup)",
           file=sys.stderr, flush=True)
@@ -453,7 +457,7 @@ def main():
             "whiflash_route + whiflash_verify_chain_early_exit" if early else
             "whiflash_route + whiflash_verify_*")
     out = {
-        "metric": "verify+route rounds/s (1 GPU); logits HBM GB/s of the verify sweep",
+        "metric": "verify+route rounds/s and logits HBM GB/s (fraction of MI355X peak), 1 GPU",
         "value": round(rounds_per_s, 2),
         "unit": "rounds/s",
         "n_gpus": 1,
@@ -467,6 +471,7 @@ def main():
         "data": "synthetic (seeded; planted-argmax logits, random trees, random router weights)",
         "config": {"workload": work.name, "mode": mode, "batch": work.B, "logits_rows": work.rows,
                    "vocab": work.V, "hidden": 2560, "router_width": 1024,
+                   "rounds_resident": len(work.pool),
                    "logits_bytes_per_round": work.logits_bytes,
                    "bytes_per_round": work.step_bytes},
         "logits_GBps": round(achieved, 1),
