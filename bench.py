@@ -52,7 +52,9 @@ def _parse():
                         "4 for the routed early-exit mode)")
     p.add_argument("--mode", choices=["fused", "separate", "early-exit", "entropy",
                                       "entropy-separate"], default="fused",
-                   help="routed workload: whiflash_round_routed, whiflash_route then "
+                   help="sweep workload: whiflash_round_chain (fused) or whiflash_route then "
+                        "whiflash_verify_chain (separate); routed workload: "
+                        "whiflash_round_routed, whiflash_route then "
                         "whiflash_verify_routed, or whiflash_round_routed_early_exit over a pool "
                         "of --pool rounds; entropy: the WhiFlash-Entropy round "
                         "whiflash_verify_routed_entropy (entropy-separate: whiflash_verify_routed "
@@ -285,6 +287,8 @@ class Sweep:
                                device=dev)
         self.ews = torch.empty(wf.early_exit_workspace_bytes(self.B, self.K, self.V),
                                dtype=torch.uint8, device=dev)
+        self.cws = torch.empty(wf.round_chain_workspace_bytes(self.B, self.m, self.K, self.V),
+                               dtype=torch.uint8, device=dev)
         self.early = False
         self.wf = wf
         self.setup_s = time.time() - t0
@@ -305,6 +309,13 @@ class Sweep:
         p = self.pool[i % len(self.pool)]
         self.wf.route(p["hidden"], self.W1, self.b1, self.W2, None, self.tau, delta_al=self.dal,
                       choice=self.choice, workspace=self.rws)
+
+    def fused_step(self, i):
+        """route + verify_chain in one call (whiflash_round_chain)."""
+        p = self.pool[i % len(self.pool)]
+        self.wf.round_chain(p["hidden"], self.W1, self.b1, self.W2, None, self.tau, p["logits"],
+                            p["draft"], row_argmax=False, delta_al=self.dal, choice=self.choice,
+                            accept_len=self.al, bonus=self.bonus, workspace=self.cws)
 
     def verify(self, i):
         p = self.pool[i % len(self.pool)]
@@ -372,8 +383,10 @@ def main():
     if entropy and not hasattr(work, "entropy_step"):
         print("--mode entropy applies to the routed workload", file=sys.stderr)
         sys.exit(2)
-    # The routed workload's early-exit step is the fused round; the chain workload has none.
-    fused = args.mode in ("fused", "early-exit") and hasattr(work, "fused_step")
+    # The routed workload's early-exit step is the fused early-exit round; the chain workload
+    # has no fused early-exit round, so its early-exit step is route + verify.
+    fused = (args.mode == "fused" and hasattr(work, "fused_step")) or \
+        (args.mode == "early-exit" and isinstance(work, Routed))
     if early:
         work.use_early_exit()
     if entropy:
@@ -453,7 +466,8 @@ def main():
     mode = ("whiflash_verify_routed_entropy" if args.mode == "entropy" else
             "whiflash_verify_routed + whiflash_route_entropy" if args.mode == "entropy-separate" else
             "whiflash_round_routed_early_exit" if fused and early else
-            "whiflash_round_routed" if fused else
+            "whiflash_round_routed" if fused and isinstance(work, Routed) else
+            "whiflash_round_chain" if fused else
             "whiflash_route + whiflash_verify_chain_early_exit" if early else
             "whiflash_route + whiflash_verify_*")
     out = {

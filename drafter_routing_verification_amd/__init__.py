@@ -22,6 +22,8 @@ Entry points (same names as the C ABI):
                           d2t, tau)   verify_routed + the entropy policy at the accepted rows
                           -> (accept_len, bonus, best_node, row_argmax, entropy, next_choice)
     catchup_update(cur_choice, accept_len, next_choice, backlog)  -> (switch_flag, catchup_len)
+    round_chain(hidden, W1, b1, W2, b2, tau, logits, draft)   route + verify_chain fused
+                 -> (delta_al, choice, accept_len, bonus, row_argmax)
     round_routed(hidden, W1, b1, W2, b2, tau, logits, row_offsets, total_rows, chain_draft,
                  parent, draft_ids, d2t)   route + verify_routed fused
                  -> (delta_al, choice, accept_len, bonus, best_node, row_argmax)
@@ -63,6 +65,9 @@ from ._binding import (  # noqa: F401
     catchup_update,
     whiflash_catchup_update,
     round_routed,
+    round_chain,
+    round_chain_workspace_bytes,
+    whiflash_round_chain,
     round_workspace_bytes,
     whiflash_round_routed,
     whiflash_route_entropy,

@@ -53,6 +53,10 @@ _SIGNATURES = {
                                                 _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_i32,
                                                 _c_f, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                                 _c_sz, _c_p]),
+    "whiflash_round_chain_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "whiflash_round_chain": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_f,
+                                      _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                      _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_verify_tree": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
                                       _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_route_gather": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p,
@@ -156,6 +160,14 @@ def whiflash_verify_routed_entropy(*args):
 
 def verify_routed_entropy_workspace_bytes(B: int, total_rows: int, V: int) -> int:
     return int(lib().whiflash_verify_routed_entropy_workspace_bytes(B, total_rows, V))
+
+
+def whiflash_round_chain(*args):
+    return lib().whiflash_round_chain(*args)
+
+
+def round_chain_workspace_bytes(B: int, m: int, K: int, V: int) -> int:
+    return int(lib().whiflash_round_chain_workspace_bytes(B, m, K, V))
 
 
 def whiflash_verify_tree(*args):
@@ -609,3 +621,49 @@ def verify_routed_entropy(logits, row_offsets, total_rows: int, choice, chain_dr
         _ptr(entropy), _ptr(next_choice), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(logits, stream)))
     return accept_len, bonus, best_node, row_argmax, entropy, next_choice
+
+
+def round_chain(hidden, W1, b1, W2, b2, tau: float, logits, draft, *, row_argmax=True,
+                delta_al=None, choice=None, accept_len=None, bonus=None, workspace=None,
+                stream=None):
+    """route + verify_chain in one call (three launches).  hidden [B, d]; logits [B*(K+1), V]
+    or [B, K+1, V]; draft [B, K] int32.  Returns (delta_al, choice, accept_len, bonus,
+    row_argmax)."""
+    _device_tensor(hidden, "hidden")
+    B, d = hidden.shape
+    m = W1.shape[0]
+    for t, name in ((hidden, "hidden"), (W1, "W1"), (W2, "W2")):
+        _device_tensor(t, name)
+        if not t.is_contiguous() or t.dtype != hidden.dtype:
+            raise TypeError(f"{name} must be contiguous with the dtype of hidden")
+    if tuple(W1.shape) != (m, d) or W2.numel() != m:
+        raise ValueError("W1 must be [m, d] and W2 hold m elements")
+    dev = hidden.device
+    if b1 is not None and (b1.dtype != torch.float32 or b1.numel() != m or not b1.is_contiguous()):
+        raise TypeError("b1 must be a contiguous float32 tensor of m elements")
+    if b2 is not None and not isinstance(b2, torch.Tensor):
+        b2 = torch.tensor([float(b2)], dtype=torch.float32, device=dev)
+    _device_tensor(draft, "draft")
+    if draft.shape[0] != B:
+        raise ValueError("draft must be [B, K] with the batch of hidden")
+    K = draft.shape[1]
+    rows = B * (K + 1)
+    V, stride = _rows_view(logits, rows)
+    _i32(draft, "draft")
+    new = lambda dt: torch.empty(B, dtype=dt, device=dev)
+    delta_al = new(torch.float32) if delta_al is None else delta_al
+    choice = new(torch.int32) if choice is None else choice
+    accept_len = new(torch.int32) if accept_len is None else accept_len
+    bonus = new(torch.int32) if bonus is None else bonus
+    if row_argmax is True:
+        row_argmax = torch.empty(rows, dtype=torch.int32, device=dev)
+    elif row_argmax is False:
+        row_argmax = None
+    ws = _workspace(workspace, round_chain_workspace_bytes(B, m, K, V), dev)
+    _check(whiflash_round_chain(_ptr(hidden), _dtype_code(hidden), d, _ptr(W1), _ptr(b1), m,
+                                _ptr(W2), _ptr(b2), float(tau), _ptr(delta_al), _ptr(choice),
+                                _ptr(logits), _dtype_code(logits), B, K, V, stride, _ptr(draft),
+                                _ptr(accept_len), _ptr(bonus), _ptr(row_argmax), _ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(),
+                                _stream(hidden, stream)))
+    return delta_al, choice, accept_len, bonus, row_argmax

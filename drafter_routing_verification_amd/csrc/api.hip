@@ -533,4 +533,53 @@ int32_t whiflash_verify_routed_entropy(const void* logits, int32_t dtype, int32_
                                           ws + part_bytes + best_bytes, stream));
 }
 
+size_t whiflash_round_chain_workspace_bytes(int32_t B, int32_t m, int32_t K, int32_t V) {
+  if (B <= 0 || m <= 0 || K < 0 || V <= 0) return 0;
+  return whiflash_route_workspace_bytes(B, m) +
+         whiflash_verify_workspace_bytes(static_cast<int32_t>(static_cast<int64_t>(B) * (K + 1)), V);
+}
+
+int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
+                             const float* b1, int32_t m, const void* W2, const float* b2,
+                             float tau, float* delta_al, int32_t* choice, const void* logits,
+                             int32_t logits_dtype, int32_t B, int32_t K, int32_t V,
+                             int64_t row_stride, const int32_t* draft, int32_t* accept_len,
+                             int32_t* bonus, int32_t* row_argmax, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  // Router arguments, as whiflash_route.
+  if (!valid_dtype(hidden_dtype)) return WF_ERR_DTYPE;
+  if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
+  // Verify arguments, as whiflash_verify_chain.
+  if (K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
+  const int64_t rows64 = static_cast<int64_t>(B) * (K + 1);
+  if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
+  const int32_t rows = static_cast<int32_t>(rows64);
+  int32_t s = check_logits(logits, logits_dtype, rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
+  if (!accept_len || !bonus || (K > 0 && !draft)) return WF_ERR_NULL;
+  if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
+    return WF_ERR_SHAPE;
+  if ((s = check_workspace(workspace, workspace_bytes,
+                           whiflash_round_chain_workspace_bytes(B, m, K, V))) != WF_OK)
+    return s;
+  const size_t route_bytes = whiflash_route_workspace_bytes(B, m);
+  float* zp = static_cast<float*>(workspace);
+  wf::Partial* part = reinterpret_cast<wf::Partial*>(static_cast<char*>(workspace) + route_bytes);
+  const wf::SweepPlan sp = wf::sweep_plan(rows, V);
+  const wf::HiddenSel direct{nullptr, nullptr, 0, 0};
+  const wf::RouterPlan plan = wf::router_plan(hidden_dtype, B, d, m, hidden, W1);
+  if (wf::launch_router_stage1(plan, hidden, direct, hidden_dtype, B, d, W1, m, zp, stream) !=
+      hipSuccess)
+    return WF_ERR_LAUNCH;
+  if (wf::launch_sweep(logits, logits_dtype, row_stride, rows, V, sp, part, stream) != hipSuccess)
+    return WF_ERR_LAUNCH;
+  return launch_status(wf::launch_round_chain_finalize(hidden_dtype, plan, zp, B, m, b1, W2, b2,
+                                                       tau, delta_al, choice, part, sp.splits, K,
+                                                       draft, accept_len, bonus, row_argmax,
+                                                       stream));
+}
+
 }  // extern "C"

@@ -163,6 +163,12 @@ hipError_t launch_catchup(int32_t B, const int32_t* cur, const int32_t* accept_l
 
 struct RoutedArgs;
 // Fused round: router finish + routed acceptance in one kernel per sequence.
+hipError_t launch_round_chain_finalize(int hidden_dtype, const RouterPlan& plan, const float* zp,
+                                       int32_t B, int32_t m, const float* b1, const void* W2,
+                                       const float* b2, float tau, float* delta_al,
+                                       int32_t* choice, const Partial* part, int32_t splits,
+                                       int32_t K, const int32_t* draft, int32_t* accept_len,
+                                       int32_t* bonus, int32_t* row_argmax, hipStream_t stream);
 hipError_t launch_round_finalize(int hidden_dtype, const RouterPlan& plan, const float* zp, int32_t B,
                                  int32_t m, const float* b1, const void* W2, const float* b2,
                                  float tau, float* delta_al, int32_t* choice,

@@ -389,6 +389,27 @@ int32_t whiflash_verify_routed_entropy(const void* logits, int32_t dtype, int32_
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 
+/* Workspace bytes of whiflash_round_chain (host-only; 0 on bad sizes). */
+size_t whiflash_round_chain_workspace_bytes(int32_t B, int32_t m, int32_t K, int32_t V);
+
+/*
+ * One DFlash round over a chain-only batch (WhiFlash paper, sections 3.2 and
+ * 3.3): whiflash_route on hidden [B, d] (its choice is the drafter for the
+ * next round) and whiflash_verify_chain on this round's logits and drafts, in
+ * three launches instead of four (router stage 1; the argmax sweep; one
+ * kernel per sequence that finishes the router and scans the chain).
+ * Arguments, layouts and errors are those of the two calls; delta_al, choice,
+ * accept_len, bonus and row_argmax equal theirs.  Workspace:
+ * whiflash_round_chain_workspace_bytes(B, m, K, V) bytes, 256-byte aligned.
+ */
+int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
+                             const float* b1, int32_t m, const void* W2, const float* b2,
+                             float tau, float* delta_al, int32_t* choice, const void* logits,
+                             int32_t logits_dtype, int32_t B, int32_t K, int32_t V,
+                             int64_t row_stride, const int32_t* draft, int32_t* accept_len,
+                             int32_t* bonus, int32_t* row_argmax, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,3 +68,45 @@ def test_round_routed_workload():
     out = _run(r, batch, dev(batch.logits), r.b2)
     _oracle(r, batch, r.b2, out)
     assert np.array_equal(out[1], batch.layout_choice) and out[2].min() >= 1
+
+
+# ------------------------------------------------------------------ chain-only round
+
+
+def _chain_round(r, cb, logits, b1, b2):
+    """whiflash_round_chain against route + verify_chain on the GPU and against the oracle."""
+    h, W1, W2 = dev(r.hidden), dev(r.W1), dev(r.W2)
+    b1d = dev(b1)
+    out = [host(x) for x in wf.round_chain(h, W1, b1d, W2, b2, r.tau, logits, dev(cb.draft))]
+    dal, ch = (host(x) for x in wf.route(h, W1, b1d, W2, b2, r.tau))
+    al, bo, rows = (host(x) for x in wf.verify_chain(logits, dev(cb.draft)))
+    assert np.all(np.abs(out[0] - dal) <= 1e-4 * np.maximum(1.0, np.abs(dal)))
+    assert np.all((out[1] == ch) | (np.abs(dal - r.tau) < 1e-3))
+    assert np.array_equal(out[2], al) and np.array_equal(out[3], bo)
+    assert np.array_equal(out[4], rows)
+    e_dal, e_ch = oracle.route(r.hidden, r.W1, b1, r.W2, np.float32(b2), r.tau, r.dtype)
+    check_router(out[0], out[1], e_dal, e_ch, r.dtype, r.tau)
+    t = oracle.row_argmax(cb.logits, cb.dtype)
+    e_al, e_bo = oracle.verify_chain(t.reshape(cb.B, cb.K + 1), cb.draft)
+    assert np.array_equal(out[4], t)
+    assert np.array_equal(out[2], e_al) and np.array_equal(out[3], e_bo)
+
+
+def test_round_chain_sweep_workload():
+    """The 256-chain throughput-sweep workload at full size (MFMA router)."""
+    print("round_chain sweep_bf16", flush=True)
+    batch, r = make_config("sweep_bf16")
+    _chain_round(r, batch, dev(batch.logits), r.b1, 0.0)
+
+
+@pytest.mark.parametrize("dtype,B,K,V", [("f32", 3, 5, 2049), ("bf16", 9, 0, 4099),
+                                          ("bf16", 40, 16, 20011)])
+def test_round_chain_small(dtype, B, K, V):
+    """GEMV and MFMA router paths, K = 0, ragged vocabularies, biases set."""
+    from synth import make_chain_batch
+    print(f"round_chain dtype={dtype} B={B} K={K} V={V}", flush=True)
+    r = make_router_inputs(B * 7 + K, B, 96 if B < 16 else 2560, 50 if B < 16 else 1024, dtype)
+    b1 = (np.random.default_rng(B).standard_normal(r.m) * 0.5).astype(np.float32)
+    cb = make_chain_batch(B + 100, B, K, V, dtype)
+    logits = padded_logits(cb.logits, (V + 7) // 8 * 8 + 8)
+    _chain_round(r, cb, logits, b1, 0.25)
