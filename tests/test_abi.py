@@ -172,3 +172,25 @@ def test_verify_chain_early_exit_validation():
     n = wf.early_exit_workspace_bytes(256, 16, V)
     assert n % 256 == 0 and n >= 256 * 4 + 256 * 17 * 8
     assert wf.early_exit_workspace_bytes(0, 16, V) == 0 and wf.early_exit_workspace_bytes(4, -1, V) == 0
+
+
+def test_round_chain_validation():
+    f = wf.whiflash_round_chain
+    # (hidden, hdt, d, W1, b1, m, W2, b2, tau, dal, ch, logits, ldt, B, K, V, stride, draft,
+    #  al, bonus, rows, ws, ws_bytes, stream)
+    ok = [ALIGNED, 1, 2560, ALIGNED, None, 1024, ALIGNED, None, 1.0, ALIGNED, ALIGNED, ALIGNED, 1,
+          256, 16, V, V, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, 1 << 30, None]
+    bad = list(ok); bad[1] = 5
+    assert f(*bad) == -3
+    bad = list(ok); bad[14] = 1024
+    assert f(*bad) == -2
+    bad = list(ok); bad[17] = None
+    assert f(*bad) == -1
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == -1
+    bad = list(ok); bad[22] = wf.round_chain_workspace_bytes(256, 1024, 16, V) - 1
+    assert f(*bad) == -5
+    bad = list(ok); bad[13] = 0
+    assert f(*bad) == 0
+    n = wf.round_chain_workspace_bytes(256, 1024, 16, V)
+    assert n == wf.route_workspace_bytes(256, 1024) + wf.verify_workspace_bytes(256 * 17, V)
