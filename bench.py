@@ -289,6 +289,9 @@ class Sweep:
                                dtype=torch.uint8, device=dev)
         self.cws = torch.empty(wf.round_chain_workspace_bytes(self.B, self.m, self.K, self.V),
                                dtype=torch.uint8, device=dev)
+        self.ecws = torch.empty(
+            wf.round_chain_early_exit_workspace_bytes(self.B, self.m, self.K, self.V),
+            dtype=torch.uint8, device=dev)
         self.early = False
         self.wf = wf
         self.setup_s = time.time() - t0
@@ -311,11 +314,12 @@ class Sweep:
                       choice=self.choice, workspace=self.rws)
 
     def fused_step(self, i):
-        """route + verify_chain in one call (whiflash_round_chain)."""
+        """route + verify_chain in one call (whiflash_round_chain, or its early-exit form)."""
         p = self.pool[i % len(self.pool)]
-        self.wf.round_chain(p["hidden"], self.W1, self.b1, self.W2, None, self.tau, p["logits"],
-                            p["draft"], row_argmax=False, delta_al=self.dal, choice=self.choice,
-                            accept_len=self.al, bonus=self.bonus, workspace=self.cws)
+        fn = self.wf.round_chain_early_exit if self.early else self.wf.round_chain
+        fn(p["hidden"], self.W1, self.b1, self.W2, None, self.tau, p["logits"], p["draft"],
+           row_argmax=False, delta_al=self.dal, choice=self.choice, accept_len=self.al,
+           bonus=self.bonus, workspace=self.ecws if self.early else self.cws)
 
     def verify(self, i):
         p = self.pool[i % len(self.pool)]
@@ -383,10 +387,8 @@ def main():
     if entropy and not hasattr(work, "entropy_step"):
         print("--mode entropy applies to the routed workload", file=sys.stderr)
         sys.exit(2)
-    # The routed workload's early-exit step is the fused early-exit round; the chain workload
-    # has no fused early-exit round, so its early-exit step is route + verify.
-    fused = (args.mode == "fused" and hasattr(work, "fused_step")) or \
-        (args.mode == "early-exit" and isinstance(work, Routed))
+    # The early-exit step of either workload is its fused early-exit round.
+    fused = args.mode in ("fused", "early-exit") and hasattr(work, "fused_step")
     if early:
         work.use_early_exit()
     if entropy:
@@ -465,7 +467,8 @@ def main():
     traffic = None if early else _traffic(work.name, work.logits_bytes)
     mode = ("whiflash_verify_routed_entropy" if args.mode == "entropy" else
             "whiflash_verify_routed + whiflash_route_entropy" if args.mode == "entropy-separate" else
-            "whiflash_round_routed_early_exit" if fused and early else
+            "whiflash_round_routed_early_exit" if fused and early and isinstance(work, Routed) else
+            "whiflash_round_chain_early_exit" if fused and early else
             "whiflash_round_routed" if fused and isinstance(work, Routed) else
             "whiflash_round_chain" if fused else
             "whiflash_route + whiflash_verify_chain_early_exit" if early else

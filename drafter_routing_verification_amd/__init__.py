@@ -67,6 +67,9 @@ from ._binding import (  # noqa: F401
     round_routed,
     round_chain,
     round_chain_workspace_bytes,
+    round_chain_early_exit,
+    round_chain_early_exit_workspace_bytes,
+    whiflash_round_chain_early_exit,
     whiflash_round_chain,
     round_workspace_bytes,
     whiflash_round_routed,

@@ -54,6 +54,11 @@ _SIGNATURES = {
                                                 _c_f, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                                 _c_sz, _c_p]),
     "whiflash_round_chain_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "whiflash_round_chain_early_exit_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "whiflash_round_chain_early_exit": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p,
+                                                 _c_p, _c_f, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                                 _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p, _c_p,
+                                                 _c_p, _c_sz, _c_p]),
     "whiflash_round_chain": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_f,
                                       _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                       _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
@@ -168,6 +173,14 @@ def whiflash_round_chain(*args):
 
 def round_chain_workspace_bytes(B: int, m: int, K: int, V: int) -> int:
     return int(lib().whiflash_round_chain_workspace_bytes(B, m, K, V))
+
+
+def whiflash_round_chain_early_exit(*args):
+    return lib().whiflash_round_chain_early_exit(*args)
+
+
+def round_chain_early_exit_workspace_bytes(B: int, m: int, K: int, V: int) -> int:
+    return int(lib().whiflash_round_chain_early_exit_workspace_bytes(B, m, K, V))
 
 
 def whiflash_verify_tree(*args):
@@ -625,7 +638,7 @@ def verify_routed_entropy(logits, row_offsets, total_rows: int, choice, chain_dr
 
 def round_chain(hidden, W1, b1, W2, b2, tau: float, logits, draft, *, row_argmax=True,
                 delta_al=None, choice=None, accept_len=None, bonus=None, workspace=None,
-                stream=None):
+                stream=None, _early=False):
     """route + verify_chain in one call (three launches).  hidden [B, d]; logits [B*(K+1), V]
     or [B, K+1, V]; draft [B, K] int32.  Returns (delta_al, choice, accept_len, bonus,
     row_argmax)."""
@@ -659,11 +672,19 @@ def round_chain(hidden, W1, b1, W2, b2, tau: float, logits, draft, *, row_argmax
         row_argmax = torch.empty(rows, dtype=torch.int32, device=dev)
     elif row_argmax is False:
         row_argmax = None
-    ws = _workspace(workspace, round_chain_workspace_bytes(B, m, K, V), dev)
-    _check(whiflash_round_chain(_ptr(hidden), _dtype_code(hidden), d, _ptr(W1), _ptr(b1), m,
+    nbytes = (round_chain_early_exit_workspace_bytes(B, m, K, V) if _early
+              else round_chain_workspace_bytes(B, m, K, V))
+    ws = _workspace(workspace, nbytes, dev)
+    fn = whiflash_round_chain_early_exit if _early else whiflash_round_chain
+    _check(fn(_ptr(hidden), _dtype_code(hidden), d, _ptr(W1), _ptr(b1), m,
                                 _ptr(W2), _ptr(b2), float(tau), _ptr(delta_al), _ptr(choice),
                                 _ptr(logits), _dtype_code(logits), B, K, V, stride, _ptr(draft),
                                 _ptr(accept_len), _ptr(bonus), _ptr(row_argmax), _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(),
                                 _stream(hidden, stream)))
     return delta_al, choice, accept_len, bonus, row_argmax
+
+
+def round_chain_early_exit(hidden, W1, b1, W2, b2, tau: float, logits, draft, **kw):
+    """round_chain with the early-exit verification (row_argmax -1 after each first mismatch)."""
+    return round_chain(hidden, W1, b1, W2, b2, tau, logits, draft, _early=True, **kw)

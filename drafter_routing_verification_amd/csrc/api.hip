@@ -582,4 +582,54 @@ int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d
                                                        stream));
 }
 
+size_t whiflash_round_chain_early_exit_workspace_bytes(int32_t B, int32_t m, int32_t K,
+                                                       int32_t V) {
+  if (B <= 0 || m <= 0 || K < 0 || V <= 0) return 0;
+  return whiflash_route_workspace_bytes(B, m) + whiflash_early_exit_workspace_bytes(B, K, V);
+}
+
+int32_t whiflash_round_chain_early_exit(const void* hidden, int32_t hidden_dtype, int32_t d,
+                                        const void* W1, const float* b1, int32_t m, const void* W2,
+                                        const float* b2, float tau, float* delta_al,
+                                        int32_t* choice, const void* logits, int32_t logits_dtype,
+                                        int32_t B, int32_t K, int32_t V, int64_t row_stride,
+                                        const int32_t* draft, int32_t* accept_len, int32_t* bonus,
+                                        int32_t* row_argmax, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(hidden_dtype)) return WF_ERR_DTYPE;
+  if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
+  if (K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
+  const int64_t rows64 = static_cast<int64_t>(B) * (K + 1);
+  if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
+  int32_t s = check_logits(logits, logits_dtype, static_cast<int32_t>(rows64), V, row_stride);
+  if (s != WF_OK) return s;
+  if (B == 0) return WF_OK;
+  if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
+  if (!accept_len || !bonus || (K > 0 && !draft)) return WF_ERR_NULL;
+  if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
+    return WF_ERR_SHAPE;
+  const wf::SweepPlan plan = wf::early_exit_plan(B, V);
+  if (rows64 * plan.splits * 1024 >= (int64_t{1} << 32)) return WF_ERR_SHAPE;
+  if ((s = check_workspace(workspace, workspace_bytes,
+                           whiflash_round_chain_early_exit_workspace_bytes(B, m, K, V))) != WF_OK)
+    return s;
+  char* ws = static_cast<char*>(workspace);
+  const size_t route_bytes = whiflash_route_workspace_bytes(B, m);
+  float* zp = reinterpret_cast<float*>(ws);
+  int* flags = reinterpret_cast<int*>(ws + route_bytes);
+  wf::Partial* part = reinterpret_cast<wf::Partial*>(
+      ws + route_bytes + round_up(static_cast<size_t>(B) * sizeof(int32_t), kWorkspaceAlign));
+  const wf::HiddenSel direct{nullptr, nullptr, 0, 0};
+  const wf::RouterPlan rplan = wf::router_plan(hidden_dtype, B, d, m, hidden, W1);
+  // Router stage 1 also clears the per-sequence mismatch flags.
+  if (wf::launch_router_stage1(rplan, hidden, direct, hidden_dtype, B, d, W1, m, zp, stream,
+                               wf::ZeroFill{flags, B}) != hipSuccess)
+    return WF_ERR_LAUNCH;
+  return launch_status(wf::launch_early_exit_round(logits, logits_dtype, row_stride, B, K, V, plan,
+                                                   draft, flags, part, hidden_dtype, rplan, zp, m,
+                                                   b1, W2, b2, tau, delta_al, choice, accept_len,
+                                                   bonus, row_argmax, stream));
+}
+
 }  // extern "C"

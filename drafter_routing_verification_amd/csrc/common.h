@@ -39,6 +39,18 @@ __device__ inline int64_t select_row(const int32_t* row0, int32_t rows_per_seq, 
   return (p >= 0 && r >= 0 && r < total_rows) ? r : -1;
 }
 
+// An int32 array a launch zeroes on the side (its first workgroup), so a later
+// launch on the same stream finds it cleared without a launch of its own.
+struct ZeroFill {
+  int32_t* p;
+  int32_t n;
+};
+
+__device__ inline void zero_fill_first_block(const ZeroFill& z) {
+  if (z.p && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < z.n; i += blockDim.x) z.p[i] = 0;
+}
+
 // Which hidden row feeds sequence b of the router: b itself (pos == NULL), or
 // the row selected by (row0, rows_per_seq, pos) among total_rows rows.
 struct HiddenSel {
@@ -106,6 +118,16 @@ hipError_t launch_early_exit_chain(const void* logits, int dtype, int64_t row_st
                                    int32_t K, int32_t V, SweepPlan plan, const int32_t* draft,
                                    int* flags, Partial* part, int32_t* accept_len, int32_t* bonus,
                                    int32_t* row_argmax, hipStream_t stream);
+// The early-exit chain round: sweep, then acceptance + router finish.  The
+// flags must already be zero (router stage 1 clears them on the side).
+struct RouterPlan;
+hipError_t launch_early_exit_round(const void* logits, int dtype, int64_t row_stride, int32_t B,
+                                   int32_t K, int32_t V, SweepPlan plan, const int32_t* draft,
+                                   int* flags, Partial* part, int hidden_dtype,
+                                   const RouterPlan& rplan, const float* zp, int32_t m,
+                                   const float* b1, const void* W2, const float* b2, float tau,
+                                   float* delta_al, int32_t* choice, int32_t* accept_len,
+                                   int32_t* bonus, int32_t* row_argmax, hipStream_t stream);
 
 hipError_t launch_finalize_chain(const Partial* part, int32_t splits, int32_t B, int32_t K,
                                  const int32_t* draft, int32_t* accept_len, int32_t* bonus,
@@ -141,7 +163,7 @@ RouterPlan router_plan(int dtype, int32_t B, int32_t d, int32_t m, const void* h
 
 hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, const HiddenSel& sel,
                                 int dtype, int32_t B, int32_t d, const void* W1, int32_t m,
-                                float* zp, hipStream_t stream);
+                                float* zp, hipStream_t stream, ZeroFill zero = ZeroFill{nullptr, 0});
 
 hipError_t launch_router_finish(const RouterPlan& plan, const HiddenSel& sel, int dtype,
                                 const float* zp, int32_t B, int32_t m, const float* b1,

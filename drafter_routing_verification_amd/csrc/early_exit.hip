@@ -136,6 +136,42 @@ __global__ __launch_bounds__(kThreads) void early_exit_accept_kernel(
     row_argmax[static_cast<int64_t>(b) * R + i] = i <= n ? t_s[i] : -1;
 }
 
+// Early-exit chain round: the acceptance above plus the router's finish for
+// sequence b (its choice is for the next round; the chain scan does not use it).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void early_exit_round_accept_kernel(
+    const float* __restrict__ zp, int KS, int B, int m, const float* __restrict__ b1,
+    const void* __restrict__ W2, const float* __restrict__ b2, float tau,
+    float* __restrict__ delta_al, int32_t* __restrict__ choice, const Partial* __restrict__ part,
+    int splits, int K, const int32_t* __restrict__ draft, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ bonus, int32_t* __restrict__ row_argmax) {
+  __shared__ int t_s[kMaxSeqRows];
+  __shared__ int n_s;
+  __shared__ float redf[kWaves];
+  const int b = blockIdx.x;
+  const int R = K + 1;
+  const HiddenSel direct{nullptr, nullptr, 0, 0};
+  const int32_t* dr = draft + static_cast<int64_t>(b) * K;
+  const int draft0 = K > 0 ? chain_load(dr, K) : -1;
+  FinishIn fin;
+  finish_load_pass<DT>(fin, zp, KS, B, m, b, 0, b1, W2);
+  MergeIn mi;
+  merge_load(mi, part, splits, b * R, R);
+  merge_finish(mi, part, splits, b * R, R, t_s, nullptr);
+  const float dal = router_finish_compute<DT>(fin, zp, direct, KS, B, m, b, b1, W2, b2, redf);
+  if (threadIdx.x == 0) {
+    delta_al[b] = dal;
+    choice[b] = dal > tau ? 1 : 0;
+  }
+  // router_finish_compute ends with a barrier, so t_s is complete here.
+  chain_accept(draft0, t_s, K, dr, accept_len + b, bonus + b, &n_s);
+  if (!row_argmax) return;
+  __syncthreads();
+  const int n = n_s;
+  for (int i = threadIdx.x; i < R; i += kThreads)
+    row_argmax[static_cast<int64_t>(b) * R + i] = i <= n ? t_s[i] : -1;
+}
+
 // ----------------------------------------------------------------- trees and routed batches
 
 // Node table of one sequence (prep kernel, one 256-thread workgroup per
@@ -323,13 +359,10 @@ SweepPlan early_exit_plan(int32_t B, int32_t V) {
   return SweepPlan{static_cast<int32_t>(splits), static_cast<int32_t>(chunk)};
 }
 
-hipError_t launch_early_exit_chain(const void* logits, int dtype, int64_t row_stride, int32_t B,
-                                   int32_t K, int32_t V, SweepPlan plan, const int32_t* draft,
-                                   int* flags, Partial* part, int32_t* accept_len, int32_t* bonus,
-                                   int32_t* row_argmax, hipStream_t stream) {
-  hipLaunchKernelGGL(early_exit_clear_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, flags, B);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+static hipError_t launch_early_exit_sweep(const void* logits, int dtype, int64_t row_stride,
+                                          int32_t B, int32_t K, int32_t V, SweepPlan plan,
+                                          const int32_t* draft, int* flags, Partial* part,
+                                          hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(B) * (K + 1) * plan.splits);
   const unsigned char* base = static_cast<const unsigned char*>(logits);
   if (dtype == WF_BF16) {
@@ -343,9 +376,42 @@ hipError_t launch_early_exit_chain(const void* logits, int dtype, int64_t row_st
                        base, row_stride * E::kBytes, V, B, K, plan.splits, plan.chunk / E::kPerVec,
                        V / E::kPerVec, draft, flags, part);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_early_exit_chain(const void* logits, int dtype, int64_t row_stride, int32_t B,
+                                   int32_t K, int32_t V, SweepPlan plan, const int32_t* draft,
+                                   int* flags, Partial* part, int32_t* accept_len, int32_t* bonus,
+                                   int32_t* row_argmax, hipStream_t stream) {
+  hipLaunchKernelGGL(early_exit_clear_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, flags, B);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (launch_early_exit_sweep(logits, dtype, row_stride, B, K, V, plan, draft, flags, part,
+                              stream) != hipSuccess)
+    return hipErrorLaunchFailure;
   hipLaunchKernelGGL(early_exit_accept_kernel, dim3(B), dim3(kThreads), 0, stream, part,
                      plan.splits, K, draft, accept_len, bonus, row_argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_early_exit_round(const void* logits, int dtype, int64_t row_stride, int32_t B,
+                                   int32_t K, int32_t V, SweepPlan plan, const int32_t* draft,
+                                   int* flags, Partial* part, int hidden_dtype,
+                                   const RouterPlan& rplan, const float* zp, int32_t m,
+                                   const float* b1, const void* W2, const float* b2, float tau,
+                                   float* delta_al, int32_t* choice, int32_t* accept_len,
+                                   int32_t* bonus, int32_t* row_argmax, hipStream_t stream) {
+  if (launch_early_exit_sweep(logits, dtype, row_stride, B, K, V, plan, draft, flags, part,
+                              stream) != hipSuccess)
+    return hipErrorLaunchFailure;
+  if (hidden_dtype == WF_BF16)
+    hipLaunchKernelGGL(early_exit_round_accept_kernel<WF_BF16>, dim3(B), dim3(kThreads), 0, stream,
+                       zp, rplan.slices, B, m, b1, W2, b2, tau, delta_al, choice, part,
+                       plan.splits, K, draft, accept_len, bonus, row_argmax);
+  else
+    hipLaunchKernelGGL(early_exit_round_accept_kernel<WF_F32>, dim3(B), dim3(kThreads), 0, stream,
+                       zp, rplan.slices, B, m, b1, W2, b2, tau, delta_al, choice, part,
+                       plan.splits, K, draft, accept_len, bonus, row_argmax);
   return hipGetLastError();
 }
 

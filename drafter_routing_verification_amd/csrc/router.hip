@@ -58,7 +58,8 @@ __device__ inline float dot16(u32x4 a, u32x4 b, float acc) {
 template <int DT, int NB, bool VEC>
 __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
     const void* __restrict__ hidden, HiddenSel sel, int B, int d, const void* __restrict__ W1, int m,
-    float* __restrict__ zp) {
+    float* __restrict__ zp, ZeroFill zero) {
+  zero_fill_first_block(zero);
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int b0 = blockIdx.y * NB;
@@ -128,7 +129,9 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
 // i = 0..3, of column l % 16.
 __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
     const unsigned short* __restrict__ hidden, HiddenSel sel, int B, int d,
-    const unsigned short* __restrict__ W1, int m, int kslice, float* __restrict__ zp) {
+    const unsigned short* __restrict__ W1, int m, int kslice, float* __restrict__ zp,
+    ZeroFill zero) {
+  zero_fill_first_block(zero);
   __shared__ __attribute__((aligned(16))) unsigned short stage[kStageRows * kStageStride];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j0 = blockIdx.x * kMfmaTileJ, bb0 = blockIdx.y * kMfmaTileB, slice = blockIdx.z;
@@ -247,41 +250,41 @@ int32_t router_max_slices(int32_t B, int32_t m) {
 
 template <int DT, int NB, bool VEC>
 static void gemv_launch(dim3 grid, hipStream_t stream, const void* hidden, const HiddenSel& sel,
-                        int32_t B, int32_t d, const void* W1, int32_t m, float* zp) {
+                        int32_t B, int32_t d, const void* W1, int32_t m, float* zp, ZeroFill zero) {
   hipLaunchKernelGGL((router_gemv_kernel<DT, NB, VEC>), grid, dim3(kThreads), 0, stream, hidden, sel,
-                     B, d, W1, m, zp);
+                     B, d, W1, m, zp, zero);
 }
 
 template <int DT, bool VEC>
 static void gemv_dispatch(const void* hidden, const HiddenSel& sel, int32_t B, int32_t d,
-                          const void* W1, int32_t m, float* zp, hipStream_t stream) {
+                          const void* W1, int32_t m, float* zp, hipStream_t stream, ZeroFill zero) {
   const unsigned gx = (m + kWaves - 1) / kWaves;
-  if (B == 1) gemv_launch<DT, 1, VEC>(dim3(gx, 1), stream, hidden, sel, B, d, W1, m, zp);
-  else if (B <= 2) gemv_launch<DT, 2, VEC>(dim3(gx, 1), stream, hidden, sel, B, d, W1, m, zp);
-  else if (B <= 4) gemv_launch<DT, 4, VEC>(dim3(gx, 1), stream, hidden, sel, B, d, W1, m, zp);
-  else gemv_launch<DT, 8, VEC>(dim3(gx, (B + 7) / 8), stream, hidden, sel, B, d, W1, m, zp);
+  if (B == 1) gemv_launch<DT, 1, VEC>(dim3(gx, 1), stream, hidden, sel, B, d, W1, m, zp, zero);
+  else if (B <= 2) gemv_launch<DT, 2, VEC>(dim3(gx, 1), stream, hidden, sel, B, d, W1, m, zp, zero);
+  else if (B <= 4) gemv_launch<DT, 4, VEC>(dim3(gx, 1), stream, hidden, sel, B, d, W1, m, zp, zero);
+  else gemv_launch<DT, 8, VEC>(dim3(gx, (B + 7) / 8), stream, hidden, sel, B, d, W1, m, zp, zero);
 }
 
 hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, const HiddenSel& sel,
                                 int dtype, int32_t B, int32_t d, const void* W1, int32_t m,
-                                float* zp, hipStream_t stream) {
+                                float* zp, hipStream_t stream, ZeroFill zero) {
   if (plan.mfma) {
     const dim3 grid((m + kMfmaTileJ - 1) / kMfmaTileJ, (B + kMfmaTileB - 1) / kMfmaTileB,
                     plan.slices);
     hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(kThreads), 0, stream,
                        static_cast<const unsigned short*>(hidden), sel, B, d,
-                       static_cast<const unsigned short*>(W1), m, plan.kslice, zp);
+                       static_cast<const unsigned short*>(W1), m, plan.kslice, zp, zero);
     return hipGetLastError();
   }
   const int per = dtype == WF_BF16 ? 8 : 4;
   const bool vec = (reinterpret_cast<uintptr_t>(hidden) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(W1) % 16 == 0) && (d % per == 0);
   if (dtype == WF_BF16) {
-    if (vec) gemv_dispatch<WF_BF16, true>(hidden, sel, B, d, W1, m, zp, stream);
-    else gemv_dispatch<WF_BF16, false>(hidden, sel, B, d, W1, m, zp, stream);
+    if (vec) gemv_dispatch<WF_BF16, true>(hidden, sel, B, d, W1, m, zp, stream, zero);
+    else gemv_dispatch<WF_BF16, false>(hidden, sel, B, d, W1, m, zp, stream, zero);
   } else {
-    if (vec) gemv_dispatch<WF_F32, true>(hidden, sel, B, d, W1, m, zp, stream);
-    else gemv_dispatch<WF_F32, false>(hidden, sel, B, d, W1, m, zp, stream);
+    if (vec) gemv_dispatch<WF_F32, true>(hidden, sel, B, d, W1, m, zp, stream, zero);
+    else gemv_dispatch<WF_F32, false>(hidden, sel, B, d, W1, m, zp, stream, zero);
   }
   return hipGetLastError();
 }

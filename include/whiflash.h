@@ -410,6 +410,28 @@ int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d
                              int32_t* bonus, int32_t* row_argmax, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes of whiflash_round_chain_early_exit (host-only; 0 on bad sizes). */
+size_t whiflash_round_chain_early_exit_workspace_bytes(int32_t B, int32_t m, int32_t K, int32_t V);
+
+/*
+ * whiflash_round_chain with the early-exit verification: whiflash_route and
+ * whiflash_verify_chain_early_exit in three launches (router stage 1, which
+ * also clears the mismatch flags; the early-exit sweep; acceptance + router
+ * finish).  Arguments and errors are those of whiflash_round_chain;
+ * delta_al, choice, accept_len, bonus and row_argmax equal those of the two
+ * calls made in turn.  Workspace:
+ * whiflash_round_chain_early_exit_workspace_bytes(B, m, K, V) bytes, 256-byte
+ * aligned; calls sharing a workspace must not overlap in time.
+ */
+int32_t whiflash_round_chain_early_exit(const void* hidden, int32_t hidden_dtype, int32_t d,
+                                        const void* W1, const float* b1, int32_t m, const void* W2,
+                                        const float* b2, float tau, float* delta_al,
+                                        int32_t* choice, const void* logits, int32_t logits_dtype,
+                                        int32_t B, int32_t K, int32_t V, int64_t row_stride,
+                                        const int32_t* draft, int32_t* accept_len, int32_t* bonus,
+                                        int32_t* row_argmax, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

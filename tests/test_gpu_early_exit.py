@@ -126,3 +126,26 @@ def test_early_exit_workloads(name, rnd):
     runs = [_run(logits, batch.draft) for _ in range(2)]
     assert all(np.array_equal(a, b) for a, b in zip(*runs))
     _check(batch.logits, batch.dtype, batch.draft, runs[0])
+
+
+@pytest.mark.parametrize("name", ["single_chain_f32", "batched_chain_bf16", "sweep_bf16"])
+def test_round_chain_early_exit(name):
+    """whiflash_round_chain_early_exit against route + verify_chain_early_exit and the oracle;
+    twice on one workspace (the flags are cleared by router stage 1 on every call)."""
+    from gpu_helpers import check_router
+    print(f"round_chain_early_exit {name}", flush=True)
+    batch, r = make_config(name)
+    logits = dev(batch.logits)
+    h, W1, W2, b1 = dev(r.hidden), dev(r.W1), dev(r.W2), dev(r.b1)
+    ws = torch.empty(wf.round_chain_early_exit_workspace_bytes(batch.B, r.m, batch.K, batch.V),
+                     dtype=torch.uint8, device="cuda:0")
+    outs = [[host(x) for x in wf.round_chain_early_exit(h, W1, b1, W2, 0.0, r.tau, logits,
+                                                        dev(batch.draft), workspace=ws)]
+            for _ in range(2)]
+    assert all(np.array_equal(a, b) for a, b in zip(*outs))
+    dal, ch, al, bo, rows = outs[0]
+    e_dal, e_ch = oracle.route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)
+    check_router(dal, ch, e_dal, e_ch, r.dtype, r.tau)
+    _check(batch.logits, batch.dtype, batch.draft, (al, bo, rows))
+    s_al, s_bo, s_rows = _run(logits, batch.draft)
+    assert np.array_equal(al, s_al) and np.array_equal(bo, s_bo) and np.array_equal(rows, s_rows)
