@@ -93,6 +93,93 @@ def _traffic(workload: str, launches_bytes: float):
     return entry.get("hbm_bytes_per_launch")
 
 
+# ----------------------------------------------------------------------------- CPU oracle baseline
+
+
+def _argmax_worker(conn, raw, dtype):
+    """Child process of the parallel CPU baseline: the oracle's row argmax over its own block
+    of logits rows, once per request on the pipe, until it is told to stop."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        while conn.recv():
+            conn.send(oracle.row_argmax(raw, dtype))
+    conn.close()
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_baseline(raw, dtype, route, accept, what, budget_s):
+    """Whole rounds of the oracle (route() -> choices; the row argmax of every logits row;
+    accept(t, choices)), timed on the host cores in two ways: one process on one thread, and
+    P processes (P - 1 children each take a contiguous block of rows for the argmax while the
+    parent runs the router, then the parent runs the acceptance).  Process start-up and the
+    hand-over of the rows to the children are outside the timed rounds."""
+    import multiprocessing as mp
+    import oracle
+    from threadpoolctl import threadpool_limits
+    rounds, spent = 0, 0.0
+    with threadpool_limits(limits=1):
+        while spent < budget_s:
+            t0 = time.perf_counter()
+            choice = route()
+            accept(oracle.row_argmax(raw, dtype), choice)
+            spent += time.perf_counter() - t0
+            rounds += 1
+    out = {"value": rounds / spent, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+           "sample": f"{rounds} whole rounds ({what}); {spent:.1f} s of CPU work on one thread",
+           "cpu_model": _cpu_model()}
+    P = min(16, len(os.sched_getaffinity(0)))
+    if P < 2:
+        return out
+    ctx = mp.get_context("spawn")
+    conns, procs = [], []
+    try:
+        for blk in np.array_split(np.arange(raw.shape[0]), P - 1):
+            parent_end, child_end = ctx.Pipe()
+            pr = ctx.Process(target=_argmax_worker, daemon=True,
+                             args=(child_end, raw[blk[0]:blk[-1] + 1], dtype))
+            pr.start()
+            conns.append(parent_end)
+            procs.append(pr)
+        for c in conns:                      # one untimed round: the children are ready
+            c.send(True)
+        for c in conns:
+            c.recv()
+        prounds, pspent = 0, 0.0
+        with threadpool_limits(limits=1):
+            while pspent < budget_s / 2:
+                t0 = time.perf_counter()
+                for c in conns:
+                    c.send(True)
+                choice = route()
+                accept(np.concatenate([c.recv() for c in conns]), choice)
+                pspent += time.perf_counter() - t0
+                prounds += 1
+    finally:
+        for c in conns:
+            try:
+                c.send(False)
+            except OSError:
+                pass
+        for pr in procs:
+            pr.join(timeout=30)
+    out["parallel"] = {"value": prounds / pspent, "unit": "rounds/s", "cores": P,
+                       "processes": P, "kind": "oracle",
+                       "sample": f"{prounds} whole rounds; {P - 1} processes split the rows for "
+                                 f"the argmax while the parent runs the router; {pspent:.1f} s"}
+    return out
+
+
 # ----------------------------------------------------------------------------- workloads
 
 
@@ -231,22 +318,17 @@ class Routed:
         """The oracle on whole rounds of this workload (router, argmax of every row, chain and
         tree acceptance), repeated until the CPU budget is spent."""
         import oracle
-        from threadpoolctl import threadpool_limits
         b, r = self.batch, self.router
-        rounds, spent = 0, 0.0
-        with threadpool_limits(limits=1):
-            while spent < budget_s:
-                t0 = time.perf_counter()
-                _, choice = oracle.route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)
-                t = oracle.row_argmax(b.logits, b.dtype)
-                oracle.verify_routed(t, b.offsets, choice, b.K, b.chain_draft, b.N, b.parent,
-                                     b.draft_ids, b.d2t, b.V)
-                spent += time.perf_counter() - t0
-                rounds += 1
-        return {"value": rounds / spent, "unit": "rounds/s", "cores": 1, "kind": "oracle",
-                "sample": f"{rounds} whole rounds (router on {b.B} hidden states, argmax of all "
-                          f"{self.rows} rows, routed acceptance); {spent:.1f} s of CPU work on "
-                          f"one thread"}
+
+        def route():
+            return oracle.route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)[1]
+
+        def accept(t, choice):
+            oracle.verify_routed(t, b.offsets, choice, b.K, b.chain_draft, b.N, b.parent,
+                                 b.draft_ids, b.d2t, b.V)
+        what = (f"router on {b.B} hidden states, argmax of all {self.rows} rows, routed "
+                "acceptance")
+        return _cpu_baseline(b.logits, b.dtype, route, accept, what, budget_s)
 
 
 class Sweep:
@@ -341,25 +423,19 @@ class Sweep:
         repeated until the CPU budget is spent."""
         import oracle
         import torch
-        from threadpoolctl import threadpool_limits
         p = self.pool[0]
         raw = p["logits"].view(torch.int16).cpu().numpy().view(np.uint16)
         draft = p["draft"].cpu().numpy()
         bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
         hidden, W1, W2, b1 = bits(p["hidden"]), bits(self.W1), bits(self.W2), self.b1.cpu().numpy()
-        rounds, spent = 0, 0.0
-        with threadpool_limits(limits=1):
-            while spent < budget_s:
-                t0 = time.perf_counter()
-                oracle.route(hidden, W1, b1, W2, 0.0, self.tau, "bf16")
-                t = oracle.row_argmax(raw, "bf16")
-                oracle.verify_chain(t.reshape(self.B, self.K + 1), draft)
-                spent += time.perf_counter() - t0
-                rounds += 1
-        return {"value": rounds / spent, "unit": "rounds/s", "cores": 1, "kind": "oracle",
-                "sample": f"{rounds} whole rounds (router on {self.B} hidden states, argmax of all "
-                          f"{self.rows} rows, chain acceptance); {spent:.1f} s of CPU work on one "
-                          f"thread"}
+
+        def route():
+            return oracle.route(hidden, W1, b1, W2, 0.0, self.tau, "bf16")[1]
+
+        def accept(t, choice):
+            oracle.verify_chain(t.reshape(self.B, self.K + 1), draft)
+        what = f"router on {self.B} hidden states, argmax of all {self.rows} rows, chain acceptance"
+        return _cpu_baseline(raw, "bf16", route, accept, what, budget_s)
 
 
 # ----------------------------------------------------------------------------- main
