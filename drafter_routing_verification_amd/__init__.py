@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
     route(hidden, W1, b1, W2, b2, tau)                    -> (delta_al, choice)
     route_gather(hidden_rows, pos, W1, b1, W2, b2, tau, row0=None, rows_per_seq=0)
                                                           -> (delta_al, choice)
+    argmax_sweep(logits)          the argmax sweep kernel alone -> (chunk max, chunk index)
     verify_chain(logits, draft)                           -> (accept_len, bonus, row_argmax)
     verify_chain_early_exit(logits, draft)                -> (accept_len, bonus, row_argmax)
     verify_tree_early_exit, verify_routed_early_exit, round_routed_early_exit: same arguments
@@ -39,6 +40,9 @@ from ._binding import (  # noqa: F401
     status_string,
     route_workspace_bytes,
     verify_workspace_bytes,
+    argmax_sweep,
+    argmax_sweep_plan,
+    whiflash_argmax_sweep,
     route,
     route_gather,
     whiflash_route_gather,

@@ -25,6 +25,8 @@ _SIGNATURES = {
     "whiflash_status_string": (ctypes.c_char_p, [_c_i32]),
     "whiflash_route_workspace_bytes": (_c_sz, [_c_i32, _c_i32]),
     "whiflash_verify_workspace_bytes": (_c_sz, [_c_i32, _c_i32]),
+    "whiflash_argmax_sweep_plan": (_c_i32, [_c_i32, _c_i32, _c_p, _c_p]),
+    "whiflash_argmax_sweep": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_sz, _c_p]),
     "whiflash_route": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_f,
                                 _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_verify_chain": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
@@ -118,9 +120,20 @@ def verify_workspace_bytes(total_rows: int, V: int) -> int:
     return int(lib().whiflash_verify_workspace_bytes(total_rows, V))
 
 
+def argmax_sweep_plan(rows: int, V: int) -> tuple[int, int]:
+    """(chunks per row, entries per chunk) of the argmax sweep over rows x V logits."""
+    chunks, elems = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().whiflash_argmax_sweep_plan(rows, V, ctypes.byref(chunks), ctypes.byref(elems)))
+    return chunks.value, elems.value
+
+
 # Raw C entry points (integers and pointers), for callers that manage their own memory.
 def whiflash_route(*args):
     return lib().whiflash_route(*args)
+
+
+def whiflash_argmax_sweep(*args):
+    return lib().whiflash_argmax_sweep(*args)
 
 
 def whiflash_verify_chain(*args):
@@ -349,6 +362,28 @@ def route_gather(hidden_rows, pos, W1, b1, W2, b2, tau: float, *, row0=None, row
                                  _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                  _stream(hidden_rows, stream)))
     return delta_al, choice
+
+
+def argmax_sweep(logits, *, rows=None, partials=None, stream=None):
+    """The argmax sweep kernel alone over logits [rows, V] (or [B, R, V]).  Returns
+    (max float32 [rows, chunks], index int32 [rows, chunks]): each chunk's largest value and
+    the lowest row index holding it, chunking from argmax_sweep_plan.  partials: optional
+    int32 tensor of at least rows * chunks * 2 elements to write into."""
+    if rows is None:
+        rows = logits.shape[0] if logits.dim() == 2 else logits.shape[0] * logits.shape[1]
+    V, stride = _rows_view(logits, rows)
+    chunks, _ = argmax_sweep_plan(rows, V)
+    need = rows * chunks * 2
+    if partials is None:
+        partials = torch.empty(need, dtype=torch.int32, device=logits.device)
+    else:
+        _i32(partials, "partials")
+        if partials.numel() < need:
+            raise ValueError(f"partials needs {need} int32 elements")
+    _check(whiflash_argmax_sweep(_ptr(logits), _dtype_code(logits), rows, V, stride,
+                                 _ptr(partials), partials.numel() * 4, _stream(logits, stream)))
+    rec = partials[:need].view(rows, chunks, 2)
+    return rec[..., 0].view(torch.float32), rec[..., 1]
 
 
 def verify_chain(logits, draft, *, row_argmax=True, accept_len=None, bonus=None, workspace=None,

@@ -71,6 +71,28 @@ size_t whiflash_verify_workspace_bytes(int32_t total_rows, int32_t V) {
   return round_up(static_cast<size_t>(total_rows) * plan.splits * sizeof(wf::Partial), kWorkspaceAlign);
 }
 
+int32_t whiflash_argmax_sweep_plan(int32_t rows, int32_t V, int32_t* chunks, int32_t* chunk_elems) {
+  if (rows < 1 || V < 1) return WF_ERR_SHAPE;
+  if (!chunks || !chunk_elems) return WF_ERR_NULL;
+  const wf::SweepPlan plan = wf::sweep_plan(rows, V);
+  *chunks = plan.splits;
+  *chunk_elems = plan.chunk;
+  return WF_OK;
+}
+
+int32_t whiflash_argmax_sweep(const void* logits, int32_t dtype, int32_t rows, int32_t V,
+                              int64_t row_stride, void* partials, size_t partials_bytes,
+                              hipStream_t stream) {
+  int32_t s = check_logits(logits, dtype, rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (rows == 0) return WF_OK;
+  const wf::SweepPlan plan = wf::sweep_plan(rows, V);
+  const size_t need = static_cast<size_t>(rows) * plan.splits * sizeof(wf::Partial);
+  if ((s = check_workspace(partials, partials_bytes, need)) != WF_OK) return s;
+  return launch_status(wf::launch_sweep(logits, dtype, row_stride, rows, V, plan,
+                                        static_cast<wf::Partial*>(partials), stream));
+}
+
 }  // extern "C"
 
 namespace {

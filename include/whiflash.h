@@ -74,6 +74,34 @@ size_t whiflash_route_workspace_bytes(int32_t B, int32_t m);
 size_t whiflash_verify_workspace_bytes(int32_t total_rows, int32_t V);
 
 /*
+ * How the argmax sweep cuts `rows` rows of V entries: every row into *chunks
+ * pieces, piece c covering entries [c * *chunk_elems, min(V, (c + 1) *
+ * *chunk_elems)).  *chunk_elems is a multiple of 256.  Host only.  Returns
+ * WF_ERR_SHAPE when rows < 1 or V < 1, WF_ERR_NULL when an output is NULL.
+ */
+int32_t whiflash_argmax_sweep_plan(int32_t rows, int32_t V, int32_t* chunks, int32_t* chunk_elems);
+
+/*
+ * The full-vocabulary argmax sweep alone: the first kernel of every verify
+ * entry point (greedy verification takes the target's most likely token at
+ * every drafted position; WhiFlash paper, section 3.2), launched by itself so
+ * that its time can be measured without the acceptance kernel, or its
+ * per-chunk results merged by the caller.
+ *   logits [rows, V] with row_stride, as in the verify entry points.
+ *   partials: device array of rows * chunks records {float max; int32 index},
+ *     8 bytes each, record r * chunks + c for chunk c of row r (chunking from
+ *     whiflash_argmax_sweep_plan): the chunk's largest value (bf16 widened
+ *     exactly to float32) and the lowest row index holding it (an index into
+ *     the row, in [0, V)).  partials_bytes >= rows * chunks * 8, base 256-byte
+ *     aligned; whiflash_verify_workspace_bytes(rows, V) bytes always suffice.
+ * rows == 0 is a no-op.  A chunk whose entries are all -inf reports -inf and
+ * its first index.
+ */
+int32_t whiflash_argmax_sweep(const void* logits, int32_t dtype, int32_t rows, int32_t V,
+                              int64_t row_stride, void* partials, size_t partials_bytes,
+                              hipStream_t stream);
+
+/*
  * Neural router + hardware-aware threshold (WhiFlash paper, section 3.3.2
  * "Neural Policy" and "Hardware-Aware Routing Decision"; Appendix A "Neural
  * Router Architecture"):

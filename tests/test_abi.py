@@ -194,3 +194,26 @@ def test_round_chain_validation():
     assert f(*bad) == 0
     n = wf.round_chain_workspace_bytes(256, 1024, 16, V)
     assert n == wf.route_workspace_bytes(256, 1024) + wf.verify_workspace_bytes(256 * 17, V)
+
+
+def test_argmax_sweep_plan_and_validation():
+    # every chunk starts inside the row, chunks are 256-aligned, and they cover the row
+    for rows, v in ((1, 7), (17, V), (4352, V), (4992, V), (3, 2049), (100000, 300)):
+        chunks, elems = wf.argmax_sweep_plan(rows, v)
+        assert chunks >= 1 and elems % 256 == 0
+        assert (chunks - 1) * elems < v <= chunks * elems
+        assert rows * chunks * 8 <= wf.verify_workspace_bytes(rows, v)
+    with pytest.raises(wf.WhiflashError):
+        wf.argmax_sweep_plan(0, V)
+    f = wf.whiflash_argmax_sweep
+    need = 4352 * 12 * 8
+    # (logits, dtype, rows, V, stride, partials, partials_bytes, stream)
+    assert f(None, 1, 4352, V, V, ALIGNED, need, None) == -1
+    assert f(ALIGNED, 7, 4352, V, V, ALIGNED, need, None) == -3
+    assert f(ALIGNED, 1, -1, V, V, ALIGNED, need, None) == -2
+    assert f(ALIGNED, 1, 4352, V, V - 8, ALIGNED, need, None) == -2
+    assert f(ALIGNED + 8, 1, 4352, V, V, ALIGNED, need, None) == -4
+    assert f(ALIGNED, 1, 4352, V, V, None, need, None) == -5
+    assert f(ALIGNED, 1, 4352, V, V, ALIGNED, need - 8, None) == -5
+    assert f(ALIGNED, 1, 4352, V, V, ALIGNED + 64, need, None) == -5
+    assert f(None, 1, 0, V, V, None, 0, None) == 0   # rows = 0: no-op
