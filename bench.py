@@ -15,6 +15,9 @@ Workloads:
       K = 16 (17 rows) and 64 EAGLE-3 trees of 61 nodes, packed into 4,992 bf16
       logits rows of 151,936 (1.517 GB per round); one step is
       whiflash_round_routed.
+  llama: the throughput sweep at Llama-3.1-8B shapes: 256 chains, K = 10, bf16
+      logits [256, 11, 128256] (722 MB per round), router 4096 -> 512 -> 1;
+      100 resident rounds.
 
 Prints one JSON line (rounds/s, logits GB/s, roofline of the argmax sweep and
 the CPU oracle baseline).
@@ -46,7 +49,9 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", choices=["sweep", "routed"], default="sweep")
+    p.add_argument("--workload", choices=["sweep", "routed", "llama"], default="sweep",
+                   help="sweep: 256 chains at Qwen3-4B shapes (default); routed: the 64/64 "
+                        "chain/tree mix; llama: 256 chains at Llama-3.1-8B shapes")
     p.add_argument("--pool", type=int, default=None,
                    help="distinct rounds resident in HBM (default: 100 for the sweep workload, "
                         "4 for the routed early-exit mode)")
@@ -197,6 +202,7 @@ class Routed:
         batch, r = make_config("routed_bf16")
         self.batch, self.router = batch, r
         self.V, self.rows, self.B = batch.V, batch.rows, batch.B
+        self.d, self.m = r.d, r.m
         T = lambda a: _to_dev(a, torch, dev)
         self.hidden, self.W1, self.W2 = T(r.hidden), T(r.W1), T(r.W2)
         self.b1 = T(r.b1)
@@ -341,20 +347,26 @@ class Routed:
 class Sweep:
     name = "sweep_bf16"
 
+    @staticmethod
+    def shape():
+        """(seed, B, K, V, d, m) of the throughput sweep at the Qwen3-4B shapes."""
+        from synth.workloads import CONFIGS, D_QWEN3, ROUTER_M, V_QWEN3
+        c = CONFIGS["sweep_bf16"]
+        return c["seed"], c["B"], c["K"], V_QWEN3, D_QWEN3, ROUTER_M
+
     def __init__(self, torch, dev, pool):
         from synth import make_chain_batch, make_router_inputs
-        from synth.workloads import CONFIGS, V_QWEN3, PLANT_BOOST
+        from synth.workloads import PLANT_BOOST
         import drafter_routing_verification_amd as wf
         t0 = time.time()
-        c = CONFIGS["sweep_bf16"]
-        self.B, self.K, self.V = c["B"], c["K"], V_QWEN3
+        seed, self.B, self.K, self.V, self.d, m = self.shape()
         self.rows = self.B * (self.K + 1)
         self.pool = []
         g = torch.Generator(device=dev)
         for rnd in range(pool):
-            cb = make_chain_batch(c["seed"], self.B, self.K, self.V, "bf16", 0.8, rnd, logits=False)
-            r = make_router_inputs(c["seed"], self.B, dtype="bf16", rnd=rnd)
-            g.manual_seed(c["seed"] * 1_000_003 + rnd)
+            cb = make_chain_batch(seed, self.B, self.K, self.V, "bf16", 0.8, rnd, logits=False)
+            r = make_router_inputs(seed, self.B, self.d, m, dtype="bf16", rnd=rnd)
+            g.manual_seed(seed * 1_000_003 + rnd)
             x = torch.randn((self.rows, self.V), generator=g, device=dev, dtype=torch.float32)
             planted = torch.from_numpy(cb.planted.reshape(-1).astype(np.int64)).to(dev)
             x[torch.arange(self.rows, device=dev), planted] += PLANT_BOOST
@@ -452,6 +464,17 @@ class Sweep:
         return _cpu_baseline(raw, "bf16", route, accept, what, budget_s)
 
 
+class LlamaSweep(Sweep):
+    """The same throughput sweep at Llama-3.1-8B shapes: DFlash blocks of 10 drafts (WhiFlash
+    paper, Appendix A, Table 7), a 128,256-token vocabulary, hidden 4096 and a router of
+    width 512 (the paper's d/8 rule)."""
+    name = "llama_sweep_bf16"
+
+    @staticmethod
+    def shape():
+        return 6, 256, 10, 128_256, 4_096, 512
+
+
 # ----------------------------------------------------------------------------- main
 
 
@@ -466,6 +489,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "routed":
         work = Routed(torch, dev, (args.pool or 4) if args.mode == "early-exit" else 1)
+    elif args.workload == "llama":
+        work = LlamaSweep(torch, dev, args.pool or 100)
     else:
         work = Sweep(torch, dev, args.pool or 100)
     stream = torch.cuda.current_stream()
@@ -584,7 +609,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; planted-argmax logits, random trees, random router weights)",
         "config": {"workload": work.name, "mode": mode, "batch": work.B, "logits_rows": work.rows,
-                   "vocab": work.V, "hidden": 2560, "router_width": 1024,
+                   "vocab": work.V, "hidden": work.d, "router_width": work.m,
                    "rounds_resident": len(work.pool),
                    "logits_bytes_per_round": work.logits_bytes,
                    "bytes_per_round": work.step_bytes},

@@ -110,3 +110,13 @@ def test_round_chain_small(dtype, B, K, V):
     cb = make_chain_batch(B + 100, B, K, V, dtype)
     logits = padded_logits(cb.logits, (V + 7) // 8 * 8 + 8)
     _chain_round(r, cb, logits, b1, 0.25)
+
+
+def test_round_chain_llama_bench_size():
+    """The benchmark's Llama-3.1-8B-shape workload at full size: 256 chains of K = 10 over a
+    128,256-token vocabulary, router 4096 -> 512 (MFMA path)."""
+    from synth import make_chain_batch
+    print("round_chain llama shapes, 256 chains", flush=True)
+    r = make_router_inputs(6, 256, 4096, 512, "bf16")
+    cb = make_chain_batch(6, 256, 10, 128256, "bf16")
+    _chain_round(r, cb, dev(cb.logits), r.b1, 0.0)
