@@ -14,31 +14,51 @@ namespace wf {
 namespace {
 
 constexpr int kSweepThreads = WF_SWEEP_THREADS;
+constexpr unsigned kXcds = 8;  // accelerator complex dies of an MI355X
 
 template <int DT>
 __global__ __launch_bounds__(kSweepThreads) void argmax_sweep_kernel(
     const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
     int chunk_vecs, int nvec, Partial* __restrict__ part) {
-  sweep_chunk<DT, kSweepThreads>(blockIdx.x, logits, row_bytes, V, splits, chunk_vecs, nvec, part);
+  // Workgroups are handed to the 8 XCDs round robin (workgroup i to XCD i % 8).
+  // Renumber them so that XCD x sweeps one contiguous range of chunks, in order:
+  // the n chunks are cut into 8 ranges of n / 8 (the first n % 8 one longer).
+  const unsigned n = gridDim.x, q = n / kXcds, r = n % kXcds;
+  const unsigned x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+  const int blk = static_cast<int>(x * q + (x < r ? x : r) + k);
+  sweep_chunk<DT, kSweepThreads>(blk, logits, row_bytes, V, splits, chunk_vecs, nvec, part);
 }
 
 }  // namespace
 
 SweepPlan sweep_plan(int32_t rows, int32_t V) {
   // 256-thread workgroups over chunks of ~12.8K elements (~25 KB of bf16),
-  // 12 per 151,936-wide row.  Same-process A/B on the 4,992-row routed and
-  // 4,352-row chain workloads (median of 5 interleaved trials): this 219.0 /
-  // 191.8 us; 512 threads over 30,720-element chunks 246.8 / 215.9 us, or
-  // 223.4 / 197.3 us with every load batch issued whole; 256 threads with
-  // whole batches 228.6 / 197.6 us.  Earlier: 2 chunks per row 219.2 us and 24
-  // chunks 244 us against 215.8 us for 12.  Small batches split further so a
+  // rounded down to an odd count per row: 11 per 151,936-wide row (13,824
+  // elements) and 11 per 128,256-wide row.  Small batches split further so a
   // launch still has about 2048 workgroups, but never below 2048 elements per
   // chunk.
+  //
+  // Same-process A/B, whole verify call, on the routed / chain / Llama-shape
+  // chain workloads (4,992 x 151,936, 4,352 x 151,936 and 2,816 x 128,256
+  // rows; median of 5 interleaved trials):
+  //   11 chunks per row, XCD-contiguous numbering   219.0 / 187.7 / 107.5 us
+  //   11 chunks per row, launch order               219.9 / 189.5 / 106.8 us
+  //   12 per 151,936-wide row (the earlier rule)    223.6 / 191.6 / 106.7 us
+  //   12, XCD-contiguous numbering                  222.6 / 189.7 / 107.4 us
+  //   13 chunks                                     222.1 / 189.7 / 107.4 us
+  //   10 chunks                                     225.5 / 195.1 / 108.8 us
+  // Chunks of 8K-11K or of 16K elements were slower still.  Before that
+  // (routed / chain workloads, 12 chunks per row at 219.0 / 191.8 us): 512
+  // threads over 30,720-element chunks 246.8 / 215.9 us, or 223.4 / 197.3 us
+  // with every load batch issued whole; 256 threads with whole batches 228.6 /
+  // 197.6 us; 2 chunks per row 219.2 us and 24 chunks 244 us (routed).
   constexpr int64_t kChunkTarget = WF_SWEEP_CHUNK;
   constexpr int64_t kMinBlocks = 2048 * 256 / kSweepThreads;
   constexpr int64_t kMinChunk = 2048;
   const int64_t max_splits = V / kMinChunk > 1 ? V / kMinChunk : 1;
   int64_t splits = (V + kChunkTarget - 1) / kChunkTarget;
+  // An odd number of chunks per row measured faster than its even neighbours.
+  if (splits > 2 && splits % 2 == 0) --splits;
   const int64_t for_blocks = (kMinBlocks + rows - 1) / (rows > 0 ? rows : 1);
   if (splits < for_blocks) splits = for_blocks;
   if (splits > max_splits) splits = max_splits;

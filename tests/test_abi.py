@@ -206,7 +206,7 @@ def test_argmax_sweep_plan_and_validation():
     with pytest.raises(wf.WhiflashError):
         wf.argmax_sweep_plan(0, V)
     f = wf.whiflash_argmax_sweep
-    need = 4352 * 12 * 8
+    need = 4352 * wf.argmax_sweep_plan(4352, V)[0] * 8
     # (logits, dtype, rows, V, stride, partials, partials_bytes, stream)
     assert f(None, 1, 4352, V, V, ALIGNED, need, None) == -1
     assert f(ALIGNED, 7, 4352, V, V, ALIGNED, need, None) == -3
