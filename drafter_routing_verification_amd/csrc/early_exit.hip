@@ -52,6 +52,12 @@
 #ifndef WF_EARLY_EXIT_CHUNK
 #define WF_EARLY_EXIT_CHUNK 51200
 #endif
+#ifndef WF_EE_TREE_GROUP_FROM
+#define WF_EE_TREE_GROUP_FROM 10
+#endif
+#ifndef WF_EE_TREE_GROUP
+#define WF_EE_TREE_GROUP 8
+#endif
 
 namespace wf {
 namespace {
@@ -64,6 +70,21 @@ namespace {
 // threads 94.9 us; the full sweep's loop form at 256 / 512 threads 99.8 /
 // 102.6 us.
 constexpr int kEeThreads = WF_EARLY_EXIT_THREADS;
+
+// From node index kTreeGroupFrom on, one tree-sweep workgroup covers the same
+// chunk of node u in kTreeGroup sequences: it reads their rows and masks in one
+// round trip and sweeps only the chunks still needed, one after another.  High
+// node indices are mostly absent (chains end at K) or rejected, so this saves
+// the dispatch and the round trip of a workgroup per skipped chunk.
+// Same-process A/B on the routed early-exit round (whole call, 64 chains of
+// K = 16 and 64 trees of 61 nodes): one workgroup per (node, sequence, chunk)
+// 82.8 us; (from, group) = (10, 8) 72.7 us; (10, 6) 72.9; (8, 8) 73.3;
+// (12, 8) 73.2; (7, 6) 73.4; (12, 12) 74.6; (17, 8) 75.9; (17, 16) 75.3;
+// (8, 4) 75.7; (6, 4) 76.1; (5, 8) 77.7; (24, 8) 77.8; (10, 32) 89.2.  The
+// same grouping on the chain-only schedule was slower (its late positions
+// still read about a third of their rows).
+constexpr int kTreeGroupFrom = WF_EE_TREE_GROUP_FROM;
+constexpr int kTreeGroup = WF_EE_TREE_GROUP;
 
 __global__ __launch_bounds__(kThreads) void early_exit_clear_kernel(int* __restrict__ flags, int B) {
   const int i = blockIdx.x * kThreads + threadIdx.x;
@@ -275,34 +296,14 @@ __global__ __launch_bounds__(kThreads) void ee_round_prep_kernel(
   ee_prep_sequence(a, b, c, p_s, mask_s);
 }
 
+// Sweeps chunk c of row `row`, node u of sequence b, and marks the children of
+// u that the chunk proves are not accepted.
 template <int DT>
-__global__ __launch_bounds__(kEeThreads) void ee_tree_sweep_kernel(EeTreeArgs a, int splits,
-                                                                    int chunk_vecs, int nvec,
-                                                                    Partial* __restrict__ part) {
-  const int per_u = a.B * splits;
-  const int u = blockIdx.x / per_u;
-  const int rem = blockIdx.x - u * per_u;
-  const int b = rem / splits;
-  const int c = rem - b * splits;
-  __shared__ int row_s;
+__device__ void ee_tree_read(const EeTreeArgs& a, int splits, int chunk_vecs, int nvec,
+                             Partial* __restrict__ part, int u, int b, int c, int row) {
   __shared__ float bv_s;
   __shared__ int bi_s;
   const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int row = tid == 0 ? a.rowmap[static_cast<int64_t>(u) * a.B + b] : 0;
-    bool hit = false;
-    if (tid < a.W) {
-      const unsigned long long m = __hip_atomic_load(&a.mask[static_cast<int64_t>(b) * a.W + tid],
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const unsigned long long an = a.anc[(static_cast<int64_t>(b) * a.Rmax + u) * a.W + tid];
-      hit = (m & an) != 0ull;
-    }
-    const bool rejected = __ballot(hit) != 0ull;
-    if (tid == 0) row_s = rejected ? -1 : row;
-  }
-  __syncthreads();
-  const int row = row_s;
-  if (row < 0) return;  // no such node, or not accepted: nothing is written
   // Edges of this sequence (one per node), consumed after the sweep.
   const int4* eb = a.edge + static_cast<int64_t>(b) * a.Rmax;
   const int4 none = make_int4(-1, -1, 0, 0);
@@ -333,6 +334,76 @@ __global__ __launch_bounds__(kEeThreads) void ee_tree_sweep_kernel(EeTreeArgs a,
       __hip_atomic_fetch_or(&mb[v >> 6], 1ull << (v & 63), __ATOMIC_RELAXED,
                             __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// Chunk c of node u in sequences b0 .. b0 + nb - 1: one round trip reads every
+// item's row and masks, then the items still needed are swept one after another.
+template <int DT>
+__device__ void ee_tree_group(const EeTreeArgs& a, int splits, int chunk_vecs, int nvec,
+                              Partial* __restrict__ part, int u, int b0, int nb, int c) {
+  __shared__ int grow_s[kTreeGroup];
+  __shared__ int grej_s[kTreeGroup];
+  const int tid = threadIdx.x;
+  if (tid < kTreeGroup) grej_s[tid] = 0;
+  __syncthreads();
+  if (tid < nb) grow_s[tid] = a.rowmap[static_cast<int64_t>(u) * a.B + b0 + tid];
+  for (int t = tid; t < nb * a.W; t += kEeThreads) {
+    const int j = t / a.W, w = t - j * a.W;
+    const int b = b0 + j;
+    const unsigned long long m = __hip_atomic_load(&a.mask[static_cast<int64_t>(b) * a.W + w],
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long an = a.anc[(static_cast<int64_t>(b) * a.Rmax + u) * a.W + w];
+    if ((m & an) != 0ull) grej_s[j] = 1;
+  }
+  __syncthreads();
+  for (int j = 0; j < nb; ++j) {
+    const int row = grow_s[j];
+    if (row < 0 || grej_s[j]) continue;  // no such node, or not accepted
+    ee_tree_read<DT>(a, splits, chunk_vecs, nvec, part, u, b0 + j, c, row);
+    __syncthreads();  // LDS of the sweep and of the edge test is reused by the next item
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kEeThreads) void ee_tree_sweep_kernel(EeTreeArgs a, int splits,
+                                                                    int chunk_vecs, int nvec,
+                                                                    Partial* __restrict__ part) {
+  const int per_u = a.B * splits;
+  const int single_u = a.Rmax < kTreeGroupFrom ? a.Rmax : kTreeGroupFrom;
+  const int single_blocks = single_u * per_u;
+  if (static_cast<int>(blockIdx.x) >= single_blocks) {
+    const int groups = (a.B + kTreeGroup - 1) / kTreeGroup;
+    const int lb = blockIdx.x - single_blocks;
+    const int gu = single_u + lb / (groups * splits);
+    const int grem = lb - (gu - single_u) * groups * splits;
+    const int g = grem / splits;
+    const int b0 = g * kTreeGroup;
+    ee_tree_group<DT>(a, splits, chunk_vecs, nvec, part, gu, b0,
+                      a.B - b0 < kTreeGroup ? a.B - b0 : kTreeGroup, grem - g * splits);
+    return;
+  }
+  const int u = blockIdx.x / per_u;
+  const int rem = blockIdx.x - u * per_u;
+  const int b = rem / splits;
+  const int c = rem - b * splits;
+  __shared__ int row_s;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int row = tid == 0 ? a.rowmap[static_cast<int64_t>(u) * a.B + b] : 0;
+    bool hit = false;
+    if (tid < a.W) {
+      const unsigned long long m = __hip_atomic_load(&a.mask[static_cast<int64_t>(b) * a.W + tid],
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long an = a.anc[(static_cast<int64_t>(b) * a.Rmax + u) * a.W + tid];
+      hit = (m & an) != 0ull;
+    }
+    const bool rejected = __ballot(hit) != 0ull;
+    if (tid == 0) row_s = rejected ? -1 : row;
+  }
+  __syncthreads();
+  const int row = row_s;
+  if (row < 0) return;  // no such node, or not accepted: nothing is written
+  ee_tree_read<DT>(a, splits, chunk_vecs, nvec, part, u, b, c, row);
 }
 
 }  // namespace
@@ -483,7 +554,12 @@ hipError_t launch_ee_round_prep(const EeTreeArgs& a, int hidden_dtype, const Rou
 
 hipError_t launch_ee_tree_sweep(const EeTreeArgs& a, SweepPlan plan, Partial* part,
                                 hipStream_t stream) {
-  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.Rmax) * a.B * plan.splits);
+  // Node indices before kTreeGroupFrom: one workgroup per (sequence, chunk);
+  // later ones: one per (group of kTreeGroup sequences, chunk).
+  const int64_t single_u = a.Rmax < kTreeGroupFrom ? a.Rmax : kTreeGroupFrom;
+  const int64_t groups = (a.B + kTreeGroup - 1) / kTreeGroup;
+  const unsigned blocks = static_cast<unsigned>(
+      (single_u * a.B + (a.Rmax - single_u) * groups) * plan.splits);
   if (a.dtype == WF_BF16) {
     using E = Elem<WF_BF16>;
     hipLaunchKernelGGL(ee_tree_sweep_kernel<WF_BF16>, dim3(blocks), dim3(kEeThreads), 0, stream, a,
