@@ -233,6 +233,7 @@ class Routed:
                                device=dev)
         self.sweep_out = torch.empty(self.rows * wf.argmax_sweep_plan(self.rows, self.V)[0] * 2,
                                      dtype=torch.int32, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
         self.fws = torch.empty(wf.round_workspace_bytes(B, r.m, self.rows, self.V),
                                dtype=torch.uint8, device=dev)
         K, N = batch.K, batch.N
@@ -277,6 +278,11 @@ class Routed:
         """The argmax sweep kernel alone over this round's logits (whiflash_argmax_sweep)."""
         p = self.pool[i % len(self.pool)]
         self.wf.argmax_sweep(p["logits"], partials=self.sweep_out)
+
+    def stream(self, i):
+        """The sweep's reads without its comparisons (whiflash_stream_read)."""
+        p = self.pool[i % len(self.pool)]
+        self.wf.stream_read(p["logits"], sink=self.sink)
 
     def verify(self, i):
         p = self.pool[i % len(self.pool)]
@@ -388,6 +394,7 @@ class Sweep:
                                device=dev)
         self.sweep_out = torch.empty(self.rows * wf.argmax_sweep_plan(self.rows, self.V)[0] * 2,
                                      dtype=torch.int32, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
         self.ews = torch.empty(wf.early_exit_workspace_bytes(self.B, self.K, self.V),
                                dtype=torch.uint8, device=dev)
         self.cws = torch.empty(wf.round_chain_workspace_bytes(self.B, self.m, self.K, self.V),
@@ -428,6 +435,11 @@ class Sweep:
         """The argmax sweep kernel alone over this round's logits (whiflash_argmax_sweep)."""
         p = self.pool[i % len(self.pool)]
         self.wf.argmax_sweep(p["logits"], partials=self.sweep_out)
+
+    def stream(self, i):
+        """The sweep's reads without its comparisons (whiflash_stream_read)."""
+        p = self.pool[i % len(self.pool)]
+        self.wf.stream_read(p["logits"], sink=self.sink)
 
     def verify(self, i):
         p = self.pool[i % len(self.pool)]
@@ -575,6 +587,8 @@ def main():
     # The dominant kernel alone: whiflash_argmax_sweep launches only the argmax sweep, on the
     # same stream, over the same resident rounds.
     sweep_s = None if early else timed_loop(work.sweep, K)
+    # A streaming-read ceiling on the same buffers: the sweep's loads without its comparisons.
+    stream_s = None if early else timed_loop(work.stream, K)
 
     ms_per_step = gpu_total_ms / K
     rounds_per_s = 1000.0 / ms_per_step
@@ -617,6 +631,13 @@ def main():
         "route_us": round(route_s * 1e6, 2),
         "verify_us": round(verify_s * 1e6, 2),
         **({} if early else {"sweep_us": round(sweep_s * 1e6, 2)}),
+        **({} if early else {"stream_read": {
+            "what": "whiflash_stream_read: the sweep's chunks and loads without its comparisons, "
+                    "back-to-back launches over the same resident rounds",
+            "us": round(stream_s * 1e6, 2),
+            "GBps": round(work.logits_bytes / stream_s / 1e9, 1),
+            "frac": round(work.logits_bytes / stream_s / 1e9 / HBM_PEAK_GBS, 4),
+            "sweep_over_stream": round(sweep_s / stream_s, 4)}}),
         "wall_ms_per_step": round(wall * 1000 / K, 5),
         "step_us": step_us,
         "mean_accept_len": round(mean_al, 3),

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     route_gather(hidden_rows, pos, W1, b1, W2, b2, tau, row0=None, rows_per_seq=0)
                                                           -> (delta_al, choice)
     argmax_sweep(logits)          the argmax sweep kernel alone -> (chunk max, chunk index)
+    stream_read(logits)           measurement aid: the sweep's reads alone -> sink word
     verify_chain(logits, draft)                           -> (accept_len, bonus, row_argmax)
     verify_chain_early_exit(logits, draft)                -> (accept_len, bonus, row_argmax)
     verify_tree_early_exit, verify_routed_early_exit, round_routed_early_exit: same arguments
@@ -43,6 +44,8 @@ from ._binding import (  # noqa: F401
     argmax_sweep,
     argmax_sweep_plan,
     whiflash_argmax_sweep,
+    stream_read,
+    whiflash_stream_read,
     route,
     route_gather,
     whiflash_route_gather,

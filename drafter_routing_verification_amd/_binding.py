@@ -27,6 +27,7 @@ _SIGNATURES = {
     "whiflash_verify_workspace_bytes": (_c_sz, [_c_i32, _c_i32]),
     "whiflash_argmax_sweep_plan": (_c_i32, [_c_i32, _c_i32, _c_p, _c_p]),
     "whiflash_argmax_sweep": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_sz, _c_p]),
+    "whiflash_stream_read": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p]),
     "whiflash_route": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_f,
                                 _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_verify_chain": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
@@ -134,6 +135,10 @@ def whiflash_route(*args):
 
 def whiflash_argmax_sweep(*args):
     return lib().whiflash_argmax_sweep(*args)
+
+
+def whiflash_stream_read(*args):
+    return lib().whiflash_stream_read(*args)
 
 
 def whiflash_verify_chain(*args):
@@ -384,6 +389,21 @@ def argmax_sweep(logits, *, rows=None, partials=None, stream=None):
                                  _ptr(partials), partials.numel() * 4, _stream(logits, stream)))
     rec = partials[:need].view(rows, chunks, 2)
     return rec[..., 0].view(torch.float32), rec[..., 1]
+
+
+def stream_read(logits, *, rows=None, sink=None, stream=None):
+    """Measurement aid: the argmax sweep's reads of logits without its comparisons (same
+    chunks, workgroups and loads).  Returns the int32 sink tensor [1] it writes (the XOR of
+    the 32-bit words of row 0's first chunk)."""
+    if rows is None:
+        rows = logits.shape[0] if logits.dim() == 2 else logits.shape[0] * logits.shape[1]
+    V, stride = _rows_view(logits, rows)
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=logits.device)
+    _i32(sink, "sink")
+    _check(whiflash_stream_read(_ptr(logits), _dtype_code(logits), rows, V, stride, _ptr(sink),
+                                _stream(logits, stream)))
+    return sink
 
 
 def verify_chain(logits, draft, *, row_argmax=True, accept_len=None, bonus=None, workspace=None,

@@ -80,6 +80,16 @@ int32_t whiflash_argmax_sweep_plan(int32_t rows, int32_t V, int32_t* chunks, int
   return WF_OK;
 }
 
+int32_t whiflash_stream_read(const void* logits, int32_t dtype, int32_t rows, int32_t V,
+                             int64_t row_stride, uint32_t* sink, hipStream_t stream) {
+  const int32_t s = check_logits(logits, dtype, rows, V, row_stride);
+  if (s != WF_OK) return s;
+  if (rows == 0) return WF_OK;
+  if (!sink) return WF_ERR_NULL;
+  return launch_status(wf::launch_stream_read(logits, dtype, row_stride, rows, V,
+                                              wf::sweep_plan(rows, V), sink, stream));
+}
+
 int32_t whiflash_argmax_sweep(const void* logits, int32_t dtype, int32_t rows, int32_t V,
                               int64_t row_stride, void* partials, size_t partials_bytes,
                               hipStream_t stream) {

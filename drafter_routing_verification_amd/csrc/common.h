@@ -66,6 +66,10 @@ __device__ inline int64_t hidden_row(const HiddenSel& s, int b) {
 
 hipError_t launch_sweep(const void* logits, int dtype, int64_t row_stride, int32_t rows, int32_t V,
                         SweepPlan plan, Partial* part, hipStream_t stream);
+// The sweep's reads alone (same chunks, workgroups and loads, no comparisons);
+// writes one word derived from chunk 0 of row 0 to *sink.
+hipError_t launch_stream_read(const void* logits, int dtype, int64_t row_stride, int32_t rows,
+                              int32_t V, SweepPlan plan, unsigned* sink, hipStream_t stream);
 
 
 // Early-exit verification of trees and routed batches (see early_exit.hip).

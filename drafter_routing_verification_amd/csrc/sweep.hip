@@ -16,17 +16,58 @@ namespace {
 constexpr int kSweepThreads = WF_SWEEP_THREADS;
 constexpr unsigned kXcds = 8;  // accelerator complex dies of an MI355X
 
+// Workgroups are handed to the 8 XCDs round robin (workgroup i to XCD i % 8).
+// Renumber them so that XCD x sweeps one contiguous range of chunks, in order:
+// the n chunks are cut into 8 ranges of n / 8 (the first n % 8 one longer).
+__device__ inline int xcd_contiguous_block() {
+  const unsigned n = gridDim.x, q = n / kXcds, r = n % kXcds;
+  const unsigned x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+  return static_cast<int>(x * q + (x < r ? x : r) + k);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kSweepThreads) void argmax_sweep_kernel(
     const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
     int chunk_vecs, int nvec, Partial* __restrict__ part) {
-  // Workgroups are handed to the 8 XCDs round robin (workgroup i to XCD i % 8).
-  // Renumber them so that XCD x sweeps one contiguous range of chunks, in order:
-  // the n chunks are cut into 8 ranges of n / 8 (the first n % 8 one longer).
-  const unsigned n = gridDim.x, q = n / kXcds, r = n % kXcds;
-  const unsigned x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
-  const int blk = static_cast<int>(x * q + (x < r ? x : r) + k);
-  sweep_chunk<DT, kSweepThreads>(blk, logits, row_bytes, V, splits, chunk_vecs, nvec, part);
+  sweep_chunk<DT, kSweepThreads>(xcd_contiguous_block(), logits, row_bytes, V, splits, chunk_vecs,
+                                 nvec, part);
+}
+
+// The sweep's reads without its comparisons: the same chunks, workgroups,
+// numbering and loads, each thread folding its data into an XOR.  Workgroup
+// 0's XOR (chunk 0 of row 0) is written to *sink so the loads stay live.
+__global__ __launch_bounds__(kSweepThreads) void stream_read_kernel(
+    const unsigned char* __restrict__ logits, int64_t row_bytes, int splits, int chunk_vecs,
+    int nvec, unsigned* __restrict__ sink) {
+  const int blk = xcd_contiguous_block();
+  const int row = blk / splits;
+  const int c = blk - row * splits;
+  const u32x4* vp = reinterpret_cast<const u32x4*>(logits + static_cast<int64_t>(row) * row_bytes);
+  const int v0 = c * chunk_vecs;
+  const int v1 = min(v0 + chunk_vecs, nvec);
+  unsigned acc = 0;
+  int v = v0 + threadIdx.x;
+  for (; v + (kUnroll - 1) * kSweepThreads < v1; v += kUnroll * kSweepThreads) {
+    u32x4 d[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) d[u] = load16(vp + v + u * kSweepThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= d[u][0] ^ d[u][1] ^ d[u][2] ^ d[u][3];
+  }
+  for (; v < v1; v += kSweepThreads) {
+    const u32x4 d = load16(vp + v);
+    acc ^= d[0] ^ d[1] ^ d[2] ^ d[3];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
+  __shared__ unsigned sx[kSweepThreads / 64];
+  if ((threadIdx.x & 63) == 0) sx[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (blk == 0 && threadIdx.x == 0) {
+    unsigned t = 0;
+    for (int w = 0; w < kSweepThreads / 64; ++w) t ^= sx[w];
+    *sink = t;
+  }
 }
 
 }  // namespace
@@ -87,6 +128,18 @@ hipError_t launch_sweep(const void* logits, int dtype, int64_t row_stride, int32
                        dim3(kSweepThreads), 0, stream, base, row_stride * E::kBytes, V, plan.splits,
                        plan.chunk / E::kPerVec, V / E::kPerVec, part);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* logits, int dtype, int64_t row_stride, int32_t rows,
+                              int32_t V, SweepPlan plan, unsigned* sink, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(rows) * plan.splits;
+  if (blocks == 0) return hipSuccess;
+  const int per = dtype == WF_BF16 ? Elem<WF_BF16>::kPerVec : Elem<WF_F32>::kPerVec;
+  const int64_t bytes = dtype == WF_BF16 ? Elem<WF_BF16>::kBytes : Elem<WF_F32>::kBytes;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kSweepThreads),
+                     0, stream, static_cast<const unsigned char*>(logits), row_stride * bytes,
+                     plan.splits, plan.chunk / per, V / per, sink);
   return hipGetLastError();
 }
 

@@ -102,6 +102,20 @@ int32_t whiflash_argmax_sweep(const void* logits, int32_t dtype, int32_t rows, i
                               hipStream_t stream);
 
 /*
+ * A measurement aid, not a step of the method: the argmax sweep's reads
+ * without its comparisons.  It reads the same whole 16-byte vectors of every
+ * row as whiflash_argmax_sweep, cut into the same chunks and with the same
+ * workgroups, launch order and load instructions, and folds them into an XOR.
+ * The time it takes is a streaming-read ceiling for the sweep on the same
+ * buffers.  Writes to *sink (device, one uint32) the XOR of the 32-bit words of
+ * row 0's first chunk (entries [0, chunk_elems) of whiflash_argmax_sweep_plan,
+ * whole vectors only).  rows == 0 is a no-op; otherwise logits and sink must
+ * not be NULL.
+ */
+int32_t whiflash_stream_read(const void* logits, int32_t dtype, int32_t rows, int32_t V,
+                             int64_t row_stride, uint32_t* sink, hipStream_t stream);
+
+/*
  * Neural router + hardware-aware threshold (WhiFlash paper, section 3.3.2
  * "Neural Policy" and "Hardware-Aware Routing Decision"; Appendix A "Neural
  * Router Architecture"):

@@ -217,3 +217,14 @@ def test_argmax_sweep_plan_and_validation():
     assert f(ALIGNED, 1, 4352, V, V, ALIGNED, need - 8, None) == -5
     assert f(ALIGNED, 1, 4352, V, V, ALIGNED + 64, need, None) == -5
     assert f(None, 1, 0, V, V, None, 0, None) == 0   # rows = 0: no-op
+
+
+def test_stream_read_validation():
+    f = wf.whiflash_stream_read
+    # (logits, dtype, rows, V, stride, sink, stream)
+    assert f(None, 1, 0, V, V, None, None) == 0          # rows = 0: no-op
+    assert f(None, 1, 4352, V, V, ALIGNED, None) == -1
+    assert f(ALIGNED, 1, 4352, V, V, None, None) == -1
+    assert f(ALIGNED, 5, 4352, V, V, ALIGNED, None) == -3
+    assert f(ALIGNED, 1, 4352, V, V - 8, ALIGNED, None) == -2
+    assert f(ALIGNED + 8, 1, 4352, V, V, ALIGNED, None) == -4

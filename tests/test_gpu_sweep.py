@@ -101,3 +101,20 @@ def test_sweep_workload_full_size():
     assert np.array_equal(_merged(vals, idx), t)
     sample = np.random.default_rng(11).choice(batch.rows, 24, replace=False)
     _check_chunks(batch.logits, "bf16", vals, idx, rows=sample)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 20011), ("bf16", 2049)])
+def test_stream_read_sink(dtype, V):
+    """The measurement aid reads what the sweep reads: its sink is the XOR of the 32-bit words of
+    row 0's first chunk (whole 16-byte vectors only)."""
+    print(f"stream read dtype={dtype} V={V}", flush=True)
+    cb = make_chain_batch(7, 4, 8, V, dtype)
+    raw = cb.logits
+    sink = host(wf.stream_read(padded_logits(raw, (V + 7) // 8 * 8 + 8)))
+    torch.cuda.synchronize()
+    _, elems = wf.argmax_sweep_plan(raw.shape[0], V)
+    per = 8 if dtype == "bf16" else 4
+    n = min(elems, V // per * per)
+    words = np.ascontiguousarray(raw[0, :n]).view(np.uint32)
+    want = np.bitwise_xor.reduce(words) if len(words) else np.uint32(0)
+    assert np.uint32(sink[0]) == np.uint32(want)
