@@ -274,10 +274,12 @@ class Routed:
         self.wf.route(self.hidden, self.W1, self.b1, self.W2, self.b2, r.tau, delta_al=self.dal,
                       choice=self.choice, workspace=self.rws)
 
-    def sweep(self, i):
-        """The argmax sweep kernel alone over this round's logits (whiflash_argmax_sweep)."""
+    def sweep(self, i, rows=None):
+        """The argmax sweep kernel alone over this round's logits (whiflash_argmax_sweep),
+        or over its first `rows` rows."""
         p = self.pool[i % len(self.pool)]
-        self.wf.argmax_sweep(p["logits"], partials=self.sweep_out)
+        self.wf.argmax_sweep(p["logits"] if rows is None else p["logits"][:rows],
+                             partials=self.sweep_out)
 
     def stream(self, i):
         """The sweep's reads without its comparisons (whiflash_stream_read)."""
@@ -431,10 +433,12 @@ class Sweep:
            row_argmax=False, delta_al=self.dal, choice=self.choice, accept_len=self.al,
            bonus=self.bonus, workspace=self.ecws if self.early else self.cws)
 
-    def sweep(self, i):
-        """The argmax sweep kernel alone over this round's logits (whiflash_argmax_sweep)."""
+    def sweep(self, i, rows=None):
+        """The argmax sweep kernel alone over this round's logits (whiflash_argmax_sweep),
+        or over its first `rows` rows."""
         p = self.pool[i % len(self.pool)]
-        self.wf.argmax_sweep(p["logits"], partials=self.sweep_out)
+        self.wf.argmax_sweep(p["logits"] if rows is None else p["logits"][:rows],
+                             partials=self.sweep_out)
 
     def stream(self, i):
         """The sweep's reads without its comparisons (whiflash_stream_read)."""
@@ -488,6 +492,20 @@ class LlamaSweep(Sweep):
 
 
 # ----------------------------------------------------------------------------- main
+
+
+def _sweep_size_fit(work, timed_loop, n):
+    """Least-squares line through the sweep kernel's durations at four launch sizes."""
+    sizes = [work.rows * q // 4 for q in (1, 2, 3, 4)]
+    us = [timed_loop(lambda i, r=r: work.sweep(i, rows=r), n) * 1e6 for r in sizes]
+    nbytes = [r * work.V * 2 for r in sizes]
+    slope, fixed = np.polyfit(np.array(nbytes, np.float64), np.array(us, np.float64), 1)
+    rate = 1e-3 / slope  # GB/s
+    return {"what": "whiflash_argmax_sweep over the first rows of each resident round, "
+                    "back-to-back launches; duration = fixed_us + bytes / steady_GBps",
+            "rows": sizes, "us": [round(u, 2) for u in us],
+            "fixed_us": round(float(fixed), 2), "steady_GBps": round(float(rate), 1),
+            "steady_frac": round(float(rate) / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -590,6 +608,11 @@ def main():
     # A streaming-read ceiling on the same buffers: the sweep's loads without its comparisons.
     stream_s = None if early else timed_loop(work.stream, K)
 
+    # The sweep kernel's fixed cost per launch (ramp-up, drain, dispatch) and its steady
+    # streaming rate: the same launches over the first quarter, half, three quarters and all
+    # of each resident round's rows, fitted as duration = fixed + bytes / rate.
+    size_fit = None if early else _sweep_size_fit(work, timed_loop, K)
+
     ms_per_step = gpu_total_ms / K
     rounds_per_s = 1000.0 / ms_per_step
     # Algorithmic bytes of the verify call: every logits row, or with the early-exit
@@ -638,6 +661,7 @@ def main():
             "GBps": round(work.logits_bytes / stream_s / 1e9, 1),
             "frac": round(work.logits_bytes / stream_s / 1e9 / HBM_PEAK_GBS, 4),
             "sweep_over_stream": round(sweep_s / stream_s, 4)}}),
+        **({} if early else {"sweep_size_fit": size_fit}),
         "wall_ms_per_step": round(wall * 1000 / K, 5),
         "step_us": step_us,
         "mean_accept_len": round(mean_al, 3),
