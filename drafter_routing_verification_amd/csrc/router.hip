@@ -30,6 +30,14 @@ constexpr int kStageRows = kMfmaTileJ + kMfmaTileB;
 constexpr int kStageStride = kChunk + 8;                      // padded row (elements)
 constexpr int kPiecesPerThread = kStageRows * (kChunk / 8) / kThreads;  // 16-byte pieces
 constexpr int kChunksInFlight = 5;  // chunks whose loads are issued together
+#ifndef WF_ROUTER_WGS
+#define WF_ROUTER_WGS 256
+#endif
+// MFMA grid size the slicing of the hidden size aims for.  On 256 sequences of
+// 2560 -> 1024 (bench step, same process, two interleaved trials): 256
+// workgroups (2 slices) route 15.8 us; 512 (4 slices, two per CU, each with one
+// load batch) 15.6 us and the same step time; 1024 (7 slices) 19.0 us.
+constexpr int64_t kRouterWorkgroups = WF_ROUTER_WGS;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -239,10 +247,10 @@ RouterPlan router_plan(int dtype, int32_t B, int32_t d, int32_t m, const void* h
 }
 
 int32_t router_max_slices(int32_t B, int32_t m) {
-  // Split the hidden size until the grid covers ~256 workgroups (one per CU).
+  // Split the hidden size until the grid covers ~kRouterWorkgroups workgroups.
   const int64_t tiles = static_cast<int64_t>((m + kMfmaTileJ - 1) / kMfmaTileJ) *
                         ((B + kMfmaTileB - 1) / kMfmaTileB);
-  int64_t ks = tiles > 0 ? 256 / tiles : 1;
+  int64_t ks = tiles > 0 ? kRouterWorkgroups / tiles : 1;
   if (ks < 1) ks = 1;
   if (ks > kMaxRouterSlices) ks = kMaxRouterSlices;
   return static_cast<int32_t>(ks);
