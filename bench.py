@@ -66,6 +66,9 @@ def _parse():
                         "then whiflash_route_entropy); sweep workload: early-exit verifies with "
                         "whiflash_verify_chain_early_exit (rows up to the first mismatch only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-size-fit", action="store_true",
+                   help="skip the sweep launches over partial rounds (profiler runs use this, so "
+                        "every argmax_sweep_kernel dispatch they record covers whole rounds)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
 
@@ -611,7 +614,7 @@ def main():
     # The sweep kernel's fixed cost per launch (ramp-up, drain, dispatch) and its steady
     # streaming rate: the same launches over the first quarter, half, three quarters and all
     # of each resident round's rows, fitted as duration = fixed + bytes / rate.
-    size_fit = None if early else _sweep_size_fit(work, timed_loop, K)
+    size_fit = None if early or args.no_size_fit else _sweep_size_fit(work, timed_loop, K)
 
     ms_per_step = gpu_total_ms / K
     rounds_per_s = 1000.0 / ms_per_step
@@ -661,7 +664,7 @@ def main():
             "GBps": round(work.logits_bytes / stream_s / 1e9, 1),
             "frac": round(work.logits_bytes / stream_s / 1e9 / HBM_PEAK_GBS, 4),
             "sweep_over_stream": round(sweep_s / stream_s, 4)}}),
-        **({} if early else {"sweep_size_fit": size_fit}),
+        **({} if size_fit is None else {"sweep_size_fit": size_fit}),
         "wall_ms_per_step": round(wall * 1000 / K, 5),
         "step_us": step_us,
         "mean_accept_len": round(mean_al, 3),
