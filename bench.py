@@ -49,9 +49,11 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", choices=["sweep", "routed", "llama"], default="sweep",
+    p.add_argument("--workload", choices=["sweep", "routed", "llama", "single"], default="sweep",
                    help="sweep: 256 chains at Qwen3-4B shapes (default); routed: the 64/64 "
-                        "chain/tree mix; llama: 256 chains at Llama-3.1-8B shapes")
+                        "chain/tree mix; llama: 256 chains at Llama-3.1-8B shapes; single: one "
+                        "sequence, K = 16, float32 logits and router (latency-bound; timed by "
+                        "replaying a captured HIP graph of the steps)")
     p.add_argument("--pool", type=int, default=None,
                    help="distinct rounds resident in HBM (default: 100 for the sweep workload, "
                         "4 for the routed early-exit mode)")
@@ -494,6 +496,200 @@ class LlamaSweep(Sweep):
         return 6, 256, 10, 128_256, 4_096, 512
 
 
+class Single:
+    """One sequence: a DFlash block of 16 drafts over 151,936 float32 logits and the router
+    2560 -> 1024 on one float32 hidden state.  A launch-latency-bound step, so its launches
+    are timed by replaying a captured HIP graph: the Python binding's per-call overhead would
+    otherwise set the pace.  The pool's rounds (16 x 20.8 MB) exceed the 256 MB Infinity Cache."""
+    name = "single_chain_f32"
+    graph = True
+
+    def __init__(self, torch, dev, pool):
+        from synth import make_config
+        import drafter_routing_verification_amd as wf
+        t0 = time.time()
+        self.pool = []
+        for rnd in range(pool):
+            batch, r = make_config("single_chain_f32", rnd=rnd)
+            self.pool.append(dict(logits=_to_dev(batch.logits, torch, dev),
+                                  draft=_to_dev(batch.draft, torch, dev),
+                                  hidden=_to_dev(r.hidden, torch, dev),
+                                  W1=_to_dev(r.W1, torch, dev), W2=_to_dev(r.W2, torch, dev),
+                                  b1=_to_dev(r.b1, torch, dev)))
+            if rnd == 0:
+                self.B, self.K, self.V = batch.B, batch.K, batch.V
+                self.d, self.m, self.tau = r.d, r.m, r.tau
+                self.router_bytes = (r.hidden.size + r.W1.size + r.W2.size + r.b1.size) * 4
+                self.host0 = (batch, r)
+        self.rows = self.B * (self.K + 1)
+        self.dal = torch.empty(self.B, dtype=torch.float32, device=dev)
+        self.choice = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.al = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.bonus = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.rws = torch.empty(wf.route_workspace_bytes(self.B, self.m), dtype=torch.uint8, device=dev)
+        self.vws = torch.empty(wf.verify_workspace_bytes(self.rows, self.V), dtype=torch.uint8,
+                               device=dev)
+        self.cws = torch.empty(wf.round_chain_workspace_bytes(self.B, self.m, self.K, self.V),
+                               dtype=torch.uint8, device=dev)
+        self.sweep_out = torch.empty(self.rows * wf.argmax_sweep_plan(self.rows, self.V)[0] * 2,
+                                     dtype=torch.int32, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.early = False
+        self.wf = wf
+        self.setup_s = time.time() - t0
+        self.logits_bytes = self.rows * self.V * 4
+        self.step_bytes = self.logits_bytes + self.router_bytes + (self.B * self.K + 4 * self.B) * 4
+
+    def fused_step(self, i):
+        """route + verify_chain in one call (whiflash_round_chain: two launches at one sequence)."""
+        p = self.pool[i % len(self.pool)]
+        self.wf.round_chain(p["hidden"], p["W1"], p["b1"], p["W2"], None, self.tau, p["logits"],
+                            p["draft"], row_argmax=False, delta_al=self.dal, choice=self.choice,
+                            accept_len=self.al, bonus=self.bonus, workspace=self.cws)
+
+    def route(self, i):
+        p = self.pool[i % len(self.pool)]
+        self.wf.route(p["hidden"], p["W1"], p["b1"], p["W2"], None, self.tau, delta_al=self.dal,
+                      choice=self.choice, workspace=self.rws)
+
+    def verify(self, i):
+        p = self.pool[i % len(self.pool)]
+        self.wf.verify_chain(p["logits"], p["draft"], row_argmax=False, accept_len=self.al,
+                             bonus=self.bonus, workspace=self.vws)
+
+    def sweep(self, i, rows=None):
+        p = self.pool[i % len(self.pool)]
+        self.wf.argmax_sweep(p["logits"] if rows is None else p["logits"][:rows],
+                             partials=self.sweep_out)
+
+    def stream(self, i):
+        p = self.pool[i % len(self.pool)]
+        self.wf.stream_read(p["logits"], sink=self.sink)
+
+    def check(self):
+        al = self.al.cpu().numpy()
+        assert al.min() >= 1 and al.max() <= self.K + 1
+        return float(al.mean())
+
+    def cpu_baseline(self, budget_s):
+        """The oracle on round 0 (router in float64, argmax of the 17 rows, chain acceptance)."""
+        import oracle
+        batch, r = self.host0
+
+        def route():
+            return oracle.route(r.hidden, r.W1, r.b1, r.W2, np.float32(r.b2), r.tau, "f32")[1]
+
+        def accept(t, choice):
+            oracle.verify_chain(t.reshape(self.B, self.K + 1), batch.draft)
+        what = f"router on one float32 hidden state, argmax of all {self.rows} float32 rows, chain acceptance"
+        return _cpu_baseline(batch.logits, "f32", route, accept, what, budget_s)
+
+
+def _graph_loop(torch, work, fn, outs, n):
+    """Average duration of fn(i) when len(work.pool) consecutive calls are captured in one HIP
+    graph and the graph is replayed back to back (n calls in all, at least one replay).  Before
+    timing, three replays are checked against eager calls: `outs` are the tensors fn writes,
+    which hold the graph's last call's results after a replay."""
+    k = len(work.pool)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(k):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(k):
+            fn(i)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        fn(k - 1)
+        torch.cuda.synchronize()
+        want = [t.clone() for t in outs]
+        for t in outs:
+            t.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(outs, want)):
+            raise RuntimeError("a graph replay differs from the eager calls")
+    reps = max(1, n // k)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * k) / 1000.0
+
+
+def _bench_graph(args, torch, work):
+    """The single-sequence line: every figure from HIP graph replay (see _graph_loop)."""
+    for i in range(args.warmup):
+        work.fused_step(i)
+    torch.cuda.synchronize()
+    mean_al = work.check()
+    k = len(work.pool)
+    reps = max(1, -(-args.steps // k))
+    steps = reps * k
+    T = lambda fn, outs: _graph_loop(torch, work, fn, outs, steps)
+    step_s = T(work.fused_step, (work.al, work.bonus, work.dal, work.choice))
+    work.check()
+    route_s = T(work.route, (work.dal, work.choice))
+    verify_s = T(work.verify, (work.al, work.bonus))
+    sweep_s = T(work.sweep, (work.sweep_out,))
+    stream_s = T(work.stream, (work.sink,))
+    # For context: the same step launched from Python, back to back.
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(steps):
+        work.fused_step(i)
+    b.record()
+    torch.cuda.synchronize()
+    python_us = a.elapsed_time(b) / steps * 1000.0
+    B_ = work.logits_bytes
+    return {
+        "metric": "verify+route rounds/s and logits HBM GB/s (fraction of MI355X peak), 1 GPU",
+        "value": round(1.0 / step_s, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; planted-argmax logits, random router weights)",
+        "config": {"workload": work.name, "mode": "whiflash_round_chain, HIP graph replay",
+                   "batch": work.B, "logits_rows": work.rows, "vocab": work.V,
+                   "hidden": work.d, "router_width": work.m, "rounds_resident": len(work.pool),
+                   "logits_bytes_per_round": B_, "bytes_per_round": work.step_bytes},
+        "logits_GBps": round(B_ / verify_s / 1e9, 1),
+        "route_us": round(route_s * 1e6, 2),
+        "verify_us": round(verify_s * 1e6, 2),
+        "sweep_us": round(sweep_s * 1e6, 2),
+        "stream_read": {"what": "whiflash_stream_read, graph replay", "us": round(stream_s * 1e6, 2),
+                        "GBps": round(B_ / stream_s / 1e9, 1),
+                        "frac": round(B_ / stream_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "python_launch_us": round(python_us, 2),
+        "mean_accept_len": round(mean_al, 3),
+        "roofline": {
+            "kernel": "argmax_sweep_kernel alone (whiflash_argmax_sweep), graph replay; bytes = "
+                      "the 17 float32 logits rows; a launch-latency-bound size",
+            "bound": "hbm",
+            "achieved": round(B_ / sweep_s / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(B_ / sweep_s / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+
+
 # ----------------------------------------------------------------------------- main
 
 
@@ -524,6 +720,19 @@ def main():
         work = Routed(torch, dev, (args.pool or 4) if args.mode == "early-exit" else 1)
     elif args.workload == "llama":
         work = LlamaSweep(torch, dev, args.pool or 100)
+    elif args.workload == "single":
+        if args.mode != "fused":
+            print("--workload single times whiflash_round_chain (--mode fused) only",
+                  file=sys.stderr)
+            sys.exit(2)
+        work = Single(torch, dev, args.pool or 16)
+        print(f"# workload {work.name}: inputs resident in HBM ({work.setup_s:.1f} s setup)",
+              file=sys.stderr, flush=True)
+        out = _bench_graph(args, torch, work)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = work.cpu_baseline(args.cpu_seconds)
+        print(json.dumps(out), flush=True)
+        return
     else:
         work = Sweep(torch, dev, args.pool or 100)
     stream = torch.cuda.current_stream()

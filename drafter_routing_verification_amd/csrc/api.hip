@@ -318,16 +318,15 @@ int32_t whiflash_round_routed(const void* hidden, int32_t hidden_dtype, int32_t 
     return s;
   float* zp = static_cast<float*>(workspace);
   wf::Partial* part = reinterpret_cast<wf::Partial*>(static_cast<char*>(workspace) + route_bytes);
-  const wf::SweepPlan sp = wf::sweep_plan(total_rows, V);
+  const wf::RouterPlan plan = wf::router_plan(hidden_dtype, B, d, m, hidden, W1);
+  const bool fused = wf::round_stage1_fused(plan, hidden_dtype, hidden, B, d, W1);
+  const wf::SweepPlan sp = fused ? wf::few_rows_plan(total_rows, V, K + 1 > N ? K + 1 : N)
+                                 : wf::sweep_plan(total_rows, V);
   const wf::RoutedArgs args{part, sp.splits, V, row_offsets, total_rows, K, chain_draft, N, parent,
                             draft_ids, d2t, Vd, accept_len, bonus, best_node, row_argmax};
-  const wf::HiddenSel direct{nullptr, nullptr, 0, 0};
-  const wf::RouterPlan plan = wf::router_plan(hidden_dtype, B, d, m, hidden, W1);
-  if (wf::launch_router_stage1(plan, hidden, direct, hidden_dtype, B, d, W1, m, zp, stream) !=
-      hipSuccess)
-    return WF_ERR_LAUNCH;
-  if (wf::launch_sweep(logits, logits_dtype, row_stride, total_rows, V, sp, part, stream) !=
-      hipSuccess)
+  if (wf::launch_round_stage1(fused, plan, hidden_dtype, hidden, B, d, W1, m, zp, logits,
+                              logits_dtype, row_stride, total_rows, V, sp, part,
+                              stream) != hipSuccess)
     return WF_ERR_LAUNCH;
   return launch_status(wf::launch_round_finalize(hidden_dtype, plan, zp, B, m, b1, W2, b2, tau,
                                                  delta_al, choice, args, stream));
@@ -600,13 +599,11 @@ int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d
   const size_t route_bytes = whiflash_route_workspace_bytes(B, m);
   float* zp = static_cast<float*>(workspace);
   wf::Partial* part = reinterpret_cast<wf::Partial*>(static_cast<char*>(workspace) + route_bytes);
-  const wf::SweepPlan sp = wf::sweep_plan(rows, V);
-  const wf::HiddenSel direct{nullptr, nullptr, 0, 0};
   const wf::RouterPlan plan = wf::router_plan(hidden_dtype, B, d, m, hidden, W1);
-  if (wf::launch_router_stage1(plan, hidden, direct, hidden_dtype, B, d, W1, m, zp, stream) !=
-      hipSuccess)
-    return WF_ERR_LAUNCH;
-  if (wf::launch_sweep(logits, logits_dtype, row_stride, rows, V, sp, part, stream) != hipSuccess)
+  const bool fused = wf::round_stage1_fused(plan, hidden_dtype, hidden, B, d, W1);
+  const wf::SweepPlan sp = fused ? wf::few_rows_plan(rows, V, K + 1) : wf::sweep_plan(rows, V);
+  if (wf::launch_round_stage1(fused, plan, hidden_dtype, hidden, B, d, W1, m, zp, logits,
+                              logits_dtype, row_stride, rows, V, sp, part, stream) != hipSuccess)
     return WF_ERR_LAUNCH;
   return launch_status(wf::launch_round_chain_finalize(hidden_dtype, plan, zp, B, m, b1, W2, b2,
                                                        tau, delta_al, choice, part, sp.splits, K,

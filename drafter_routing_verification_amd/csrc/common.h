@@ -189,6 +189,20 @@ hipError_t launch_catchup(int32_t B, const int32_t* cur, const int32_t* accept_l
 
 struct RoutedArgs;
 // Fused round: router finish + routed acceptance in one kernel per sequence.
+// A fused round runs router stage 1 and the argmax sweep in one launch when the
+// router takes the GEMV path for at most 8 sequences with 16-byte aligned
+// operands; its sweep then uses few_rows_plan, whose chunk count lets the final
+// kernel merge every row of a sequence (at most rows_per_seq rows) in one pass.
+bool round_stage1_fused(const RouterPlan& plan, int hidden_dtype, const void* hidden, int32_t B,
+                        int32_t d, const void* W1);
+SweepPlan few_rows_plan(int32_t rows, int32_t V, int32_t rows_per_seq);
+// Router stage 1 and the sweep: one launch if `fused`, else the two launches of
+// launch_router_stage1 and launch_sweep.
+hipError_t launch_round_stage1(bool fused, const RouterPlan& plan, int hidden_dtype,
+                               const void* hidden, int32_t B, int32_t d, const void* W1, int32_t m,
+                               float* zp, const void* logits, int logits_dtype, int64_t row_stride,
+                               int32_t rows, int32_t V, SweepPlan sp, Partial* part,
+                               hipStream_t stream);
 hipError_t launch_round_chain_finalize(int hidden_dtype, const RouterPlan& plan, const float* zp,
                                        int32_t B, int32_t m, const float* b1, const void* W2,
                                        const float* b2, float tau, float* delta_al,

@@ -5,11 +5,15 @@
 // whiflash_verify_routed, in three launches instead of four: router stage 1,
 // the argmax sweep, then one kernel per sequence that finishes the router
 // (Delta-AL and the drafter choice) and verifies the sequence with it.
-// (Running the router's workgroups inside the sweep's launch was measured
-// slower: latency-bound router tiles stretched the 217 us sweep to 245 us.)
+// (Running the router's MFMA workgroups inside the sweep's launch was measured
+// slower: latency-bound router tiles stretched the 217 us sweep to 245 us.  For
+// a few sequences on the GEMV router path, router stage 1 and the sweep do
+// share one launch: two launches per round instead of three.)
 #include "accept.h"
 #include "common.h"
+#include "gemv_body.h"
 #include "router_math.h"
+#include "sweep_body.h"
 
 namespace wf {
 namespace {
@@ -71,7 +75,113 @@ __global__ __launch_bounds__(kThreads) void round_chain_finalize_kernel(
   chain_accept(draft0, t_s, K, dr, accept_len + b, bonus + b, nullptr);
 }
 
+// First launch of a small-batch round: workgroups [0, router_blocks) run the
+// router's GEMV tiles (workgroup i: hidden units 4 (i % router_gx) .. + 3 for
+// every sequence, all B <= NB of them), the rest run the argmax sweep's chunks.
+// The two halves read disjoint inputs and write disjoint outputs.  At a few
+// sequences both are small and latency-bound, so one launch instead of two
+// saves a launch floor; at large batches the router runs on MFMA tiles in a
+// launch of its own (router tiles inside the sweep's launch measured slower).
+template <int DTL, int DTH, int NB>
+__global__ __launch_bounds__(kThreads) void router_sweep_kernel(
+    const void* __restrict__ hidden, int B, int d, const void* __restrict__ W1, int m,
+    float* __restrict__ zp, int router_gx, int router_blocks,
+    const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
+    int chunk_vecs, int nvec, Partial* __restrict__ part) {
+  const int i = blockIdx.x;
+  if (i < router_blocks) {
+    const HiddenSel direct{nullptr, nullptr, 0, 0};
+    gemv_tile<DTH, NB, true>(i % router_gx, 0, hidden, direct, B, d, W1, m, zp);
+  } else {
+    // Few rows, few workgroups per CU: each thread issues its whole batch of loads at once.
+    sweep_chunk<DTL, kThreads, true>(i - router_blocks, logits, row_bytes, V, splits, chunk_vecs,
+                                     nvec, part);
+  }
+}
+
+template <int DTL, int DTH>
+hipError_t launch_router_sweep_nb(unsigned grid, int nb, const void* hidden, int B, int d,
+                                  const void* W1, int m, float* zp, int router_gx,
+                                  int router_blocks, const unsigned char* logits,
+                                  int64_t row_bytes, int V, int splits, int chunk_vecs, int nvec,
+                                  Partial* part, hipStream_t stream) {
+#define WF_ROUTER_SWEEP(NBV)                                                                   \
+  hipLaunchKernelGGL((router_sweep_kernel<DTL, DTH, NBV>), dim3(grid), dim3(kThreads), 0, stream, \
+                     hidden, B, d, W1, m, zp, router_gx, router_blocks, logits, row_bytes, V,   \
+                     splits, chunk_vecs, nvec, part)
+  if (nb == 1) WF_ROUTER_SWEEP(1);
+  else if (nb == 2) WF_ROUTER_SWEEP(2);
+  else if (nb == 4) WF_ROUTER_SWEEP(4);
+  else WF_ROUTER_SWEEP(8);
+#undef WF_ROUTER_SWEEP
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool round_stage1_fused(const RouterPlan& plan, int hidden_dtype, const void* hidden, int32_t B,
+                        int32_t d, const void* W1) {
+  const int per_h = hidden_dtype == WF_BF16 ? 8 : 4;
+  const bool vec = (reinterpret_cast<uintptr_t>(hidden) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(W1) % 16 == 0) && (d % per_h == 0);
+  return !plan.mfma && vec && B <= 8;
+}
+
+SweepPlan few_rows_plan(int32_t rows, int32_t V, int32_t rows_per_seq) {
+  // The final kernel merges a sequence's partials with groups of G lanes per row
+  // (G a power of two), 256 / G rows per pass, kMergePer partials per lane.  With
+  // at most kMergePer * G chunks per row and G <= 256 / rows_per_seq, every row
+  // of a sequence is merged in the first pass, from one round of loads.
+  SweepPlan p = sweep_plan(rows, V);
+  int G = 1;
+  while (2 * G * (rows_per_seq > 0 ? rows_per_seq : 1) <= kThreads && G < 64) G <<= 1;
+  const int cap = kMergePer * G;
+  if (p.splits > cap) {
+    int64_t chunk = (static_cast<int64_t>(V) + cap - 1) / cap;
+    chunk = (chunk + 255) / 256 * 256;
+    p.chunk = static_cast<int32_t>(chunk);
+    p.splits = static_cast<int32_t>((V + chunk - 1) / chunk);
+  }
+  return p;
+}
+
+hipError_t launch_round_stage1(bool fused, const RouterPlan& plan, int hidden_dtype,
+                               const void* hidden, int32_t B, int32_t d, const void* W1, int32_t m,
+                               float* zp, const void* logits, int logits_dtype, int64_t row_stride,
+                               int32_t rows, int32_t V, SweepPlan sp, Partial* part,
+                               hipStream_t stream) {
+  const int64_t router_gx = (static_cast<int64_t>(m) + kWaves - 1) / kWaves;
+  const int64_t sweep_blocks = static_cast<int64_t>(rows) * sp.splits;
+  if (!fused || router_gx + sweep_blocks > INT32_MAX) {
+    const HiddenSel direct{nullptr, nullptr, 0, 0};
+    if (launch_router_stage1(plan, hidden, direct, hidden_dtype, B, d, W1, m, zp, stream) !=
+        hipSuccess)
+      return hipErrorLaunchFailure;
+    return launch_sweep(logits, logits_dtype, row_stride, rows, V, sp, part, stream);
+  }
+  const int nb = B == 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;
+  const unsigned grid = static_cast<unsigned>(router_gx + sweep_blocks);
+  const unsigned char* base = static_cast<const unsigned char*>(logits);
+  const int gx = static_cast<int>(router_gx);
+  if (logits_dtype == WF_BF16) {
+    using E = Elem<WF_BF16>;
+    const int64_t rb = row_stride * E::kBytes;
+    const int cv = sp.chunk / E::kPerVec, nv = V / E::kPerVec;
+    return hidden_dtype == WF_BF16
+               ? launch_router_sweep_nb<WF_BF16, WF_BF16>(grid, nb, hidden, B, d, W1, m, zp, gx, gx,
+                                                          base, rb, V, sp.splits, cv, nv, part, stream)
+               : launch_router_sweep_nb<WF_BF16, WF_F32>(grid, nb, hidden, B, d, W1, m, zp, gx, gx,
+                                                         base, rb, V, sp.splits, cv, nv, part, stream);
+  }
+  using E = Elem<WF_F32>;
+  const int64_t rb = row_stride * E::kBytes;
+  const int cv = sp.chunk / E::kPerVec, nv = V / E::kPerVec;
+  return hidden_dtype == WF_BF16
+             ? launch_router_sweep_nb<WF_F32, WF_BF16>(grid, nb, hidden, B, d, W1, m, zp, gx, gx,
+                                                       base, rb, V, sp.splits, cv, nv, part, stream)
+             : launch_router_sweep_nb<WF_F32, WF_F32>(grid, nb, hidden, B, d, W1, m, zp, gx, gx,
+                                                      base, rb, V, sp.splits, cv, nv, part, stream);
+}
 
 hipError_t launch_round_finalize(int hidden_dtype, const RouterPlan& plan, const float* zp, int32_t B,
                                  int32_t m, const float* b1, const void* W2, const float* b2,

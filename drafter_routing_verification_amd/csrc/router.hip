@@ -17,12 +17,12 @@
 #include <math.h>
 
 #include "common.h"
+#include "gemv_body.h"
 #include "router_math.h"
 
 namespace wf {
 namespace {
 
-constexpr int kGemvUnroll = 4;      // 16-byte vectors in flight per lane in the GEMV
 constexpr int kMfmaTileJ = 32;      // hidden units per MFMA workgroup tile
 constexpr int kMfmaTileB = 64;      // sequences per MFMA workgroup tile
 constexpr int kChunk = 128;         // hidden-size columns staged through LDS at a time
@@ -39,91 +39,16 @@ constexpr int kChunksInFlight = 5;  // chunks whose loads are issued together
 // load batch) 15.6 us and the same step time; 1024 (7 slices) 19.0 us.
 constexpr int64_t kRouterWorkgroups = WF_ROUTER_WGS;
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Dot product of two 16-byte vectors, accumulated in float32.
-template <int DT>
-__device__ inline float dot16(u32x4 a, u32x4 b, float acc) {
-  if constexpr (DT == WF_BF16) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc = fmaf(__uint_as_float(a[q] << 16), __uint_as_float(b[q] << 16), acc);
-      acc = fmaf(__uint_as_float(a[q] & 0xffff0000u), __uint_as_float(b[q] & 0xffff0000u), acc);
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(a[q]), __uint_as_float(b[q]), acc);
-  }
-  return acc;
-}
-
-// One wave per hidden unit j and NB sequences: row j of W1 is streamed once;
-// writes zp[b][j] = W1[j] . h_b.
-// VEC: rows are 16-byte aligned and d is a multiple of the vector width, so
-// each lane reads 16-byte vectors, kGemvUnroll of them in flight.
+// One wave per hidden unit j and NB sequences (gemv_tile in gemv_body.h).
 template <int DT, int NB, bool VEC>
 __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
     const void* __restrict__ hidden, HiddenSel sel, int B, int d, const void* __restrict__ W1, int m,
     float* __restrict__ zp, ZeroFill zero) {
   zero_fill_first_block(zero);
-  const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int b0 = blockIdx.y * NB;
-  if (j >= m) return;
-  const int nb = min(NB, B - b0);
-  // Hidden row of each of this wave's sequences (-1: no valid row, dot stays 0).
-  int64_t hrow[NB];
-#pragma unroll
-  for (int q = 0; q < NB; ++q) hrow[q] = q < nb ? hidden_row(sel, b0 + q) : -1;
-  float acc[NB];
-#pragma unroll
-  for (int q = 0; q < NB; ++q) acc[q] = 0.f;
-  if constexpr (VEC) {
-    constexpr int kPer = DT == WF_BF16 ? 8 : 4;
-    const int nv = d / kPer;
-    const u32x4* wr = reinterpret_cast<const u32x4*>(W1) + static_cast<int64_t>(j) * nv;
-    const u32x4* hb = reinterpret_cast<const u32x4*>(hidden);
-    int v = lane;
-    for (; v + (kGemvUnroll - 1) * 64 < nv; v += kGemvUnroll * 64) {
-      u32x4 w[kGemvUnroll];
-#pragma unroll
-      for (int u = 0; u < kGemvUnroll; ++u) w[u] = wr[v + u * 64];
-#pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        if (hrow[q] >= 0) {
-          const u32x4* hr = hb + hrow[q] * nv;
-          u32x4 h[kGemvUnroll];
-#pragma unroll
-          for (int u = 0; u < kGemvUnroll; ++u) h[u] = hr[v + u * 64];
-#pragma unroll
-          for (int u = 0; u < kGemvUnroll; ++u) acc[q] = dot16<DT>(w[u], h[u], acc[q]);
-        }
-      }
-    }
-    for (; v < nv; v += 64) {
-      const u32x4 w = wr[v];
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-        if (hrow[q] >= 0) acc[q] = dot16<DT>(w, hb[hrow[q] * nv + v], acc[q]);
-    }
-  } else {
-    const int64_t wrow = static_cast<int64_t>(j) * d;
-    for (int k = lane; k < d; k += 64) {
-      const float w = load_elem<DT>(W1, wrow + k);
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-        if (hrow[q] >= 0) acc[q] = fmaf(w, load_elem<DT>(hidden, hrow[q] * d + k), acc[q]);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < NB; ++q) {
-    float s = acc[q];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == q && q < nb) zp[static_cast<int64_t>(b0 + q) * m + j] = s;
-  }
+  gemv_tile<DT, NB, VEC>(blockIdx.x, blockIdx.y, hidden, sel, B, d, W1, m, zp);
 }
 
 // One workgroup = 4 waves per 32 (j) x 64 (b) tile of z^T and one slice

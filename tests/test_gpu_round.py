@@ -48,7 +48,11 @@ def _oracle(r, rb, b2, out):
     return far
 
 
-@pytest.mark.parametrize("B,d,m", [(12, 256, 64), (40, 2560, 1024), (16, 104, 70), (70, 512, 50)])
+# B <= 8 with a GEMV router and 16-byte aligned operands runs router stage 1 and the sweep
+# in one launch; (8, 100, 33) has rows of 100 bf16 values (not 16-byte multiples), which
+# keeps them in two launches, as B > 8 and the MFMA router do.
+@pytest.mark.parametrize("B,d,m", [(12, 256, 64), (40, 2560, 1024), (16, 104, 70), (70, 512, 50),
+                                   (1, 256, 64), (3, 2560, 320), (5, 2560, 1024), (8, 100, 33)])
 def test_round_small(B, d, m):
     print(f"round B={B} d={d} m={m}", flush=True)
     r = make_router_inputs(B + 5, B, d, m, "bf16")
@@ -110,6 +114,29 @@ def test_round_chain_small(dtype, B, K, V):
     cb = make_chain_batch(B + 100, B, K, V, dtype)
     logits = padded_logits(cb.logits, (V + 7) // 8 * 8 + 8)
     _chain_round(r, cb, logits, b1, 0.25)
+
+
+@pytest.mark.parametrize("hd,ld,B", [("f32", "f32", 1), ("bf16", "bf16", 1), ("f32", "bf16", 2),
+                                     ("bf16", "f32", 4), ("bf16", "bf16", 5), ("f32", "f32", 8),
+                                     ("bf16", "bf16", 9)])
+def test_round_chain_few_sequences(hd, ld, B):
+    """Up to 8 sequences on the GEMV router: router stage 1 and the sweep share one launch
+    (B = 9 takes two), for every hidden / logits element-type pair."""
+    from synth import make_chain_batch
+    print(f"round_chain few sequences hidden={hd} logits={ld} B={B}", flush=True)
+    r = make_router_inputs(B + 300, B, 2560, 1024, hd)
+    b1 = (np.random.default_rng(B + 1).standard_normal(r.m) * 0.5).astype(np.float32)
+    V = 20011
+    cb = make_chain_batch(B + 301, B, 16, V, ld)
+    _chain_round(r, cb, padded_logits(cb.logits, (V + 7) // 8 * 8 + 8), b1, -0.125)
+
+
+def test_round_chain_single_sequence_f32():
+    """The single-sequence float32 workload at full size: K = 16 over 151,936 float32 logits
+    and the 2560 -> 1024 router on one float32 hidden state."""
+    print("round_chain single_chain_f32", flush=True)
+    batch, r = make_config("single_chain_f32")
+    _chain_round(r, batch, dev(batch.logits), r.b1, 0.0)
 
 
 def test_round_chain_llama_bench_size():
