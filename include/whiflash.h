@@ -265,7 +265,10 @@ size_t whiflash_round_workspace_bytes(int32_t B, int32_t m, int32_t total_rows, 
  * the same arguments, results and error codes as the two calls (hidden_dtype
  * is the router's element type, logits_dtype the logits').  It runs in three
  * launches instead of four: router stage 1, the argmax sweep, then one kernel
- * per sequence that finishes the router and verifies the sequence.  Callers
+ * per sequence that finishes the router and verifies the sequence.  With at
+ * most 8 sequences, 16-byte aligned hidden and W1 and d a multiple of 16 bytes
+ * of elements (the router's GEMV path), router stage 1 and the sweep share one
+ * launch: two in all.  Callers
  * that cannot fuse the two steps (e.g. a different stream for each) use the
  * separate entry points.
  */
@@ -439,7 +442,9 @@ size_t whiflash_round_chain_workspace_bytes(int32_t B, int32_t m, int32_t K, int
  * 3.3): whiflash_route on hidden [B, d] (its choice is the drafter for the
  * next round) and whiflash_verify_chain on this round's logits and drafts, in
  * three launches instead of four (router stage 1; the argmax sweep; one
- * kernel per sequence that finishes the router and scans the chain).
+ * kernel per sequence that finishes the router and scans the chain), or two
+ * when router stage 1 and the sweep share a launch (as in whiflash_round_routed:
+ * at most 8 sequences on the router's GEMV path).
  * Arguments, layouts and errors are those of the two calls; delta_al, choice,
  * accept_len, bonus and row_argmax equal theirs.  Workspace:
  * whiflash_round_chain_workspace_bytes(B, m, K, V) bytes, 256-byte aligned.
