@@ -173,7 +173,7 @@ int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int3
   if (!accept_len || !bonus || (K > 0 && !draft)) return WF_ERR_NULL;
   const size_t need = whiflash_verify_workspace_bytes(rows, V);
   if ((s = check_workspace(workspace, workspace_bytes, need)) != WF_OK) return s;
-  const wf::SweepPlan plan = wf::sweep_plan(rows, V);
+  const wf::SweepPlan plan = wf::few_rows_plan(rows, V, K + 1);
   wf::Partial* part = static_cast<wf::Partial*>(workspace);
   if (wf::launch_sweep(logits, dtype, row_stride, rows, V, plan, part, stream) != hipSuccess)
     return WF_ERR_LAUNCH;
@@ -230,7 +230,7 @@ int32_t whiflash_verify_tree(const void* logits, int32_t dtype, int32_t B, int32
   if (!parent || !draft_ids || !d2t || !accept_len || !bonus) return WF_ERR_NULL;
   const size_t need = whiflash_verify_workspace_bytes(rows, V);
   if ((s = check_workspace(workspace, workspace_bytes, need)) != WF_OK) return s;
-  const wf::SweepPlan plan = wf::sweep_plan(rows, V);
+  const wf::SweepPlan plan = wf::few_rows_plan(rows, V, N);
   wf::Partial* part = static_cast<wf::Partial*>(workspace);
   if (wf::launch_sweep(logits, dtype, row_stride, rows, V, plan, part, stream) != hipSuccess)
     return WF_ERR_LAUNCH;
@@ -257,7 +257,7 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
     return WF_ERR_NULL;
   const size_t need = whiflash_verify_workspace_bytes(total_rows, V);
   if ((s = check_workspace(workspace, workspace_bytes, need)) != WF_OK) return s;
-  const wf::SweepPlan plan = wf::sweep_plan(total_rows, V);
+  const wf::SweepPlan plan = wf::few_rows_plan(total_rows, V, K + 1 > N ? K + 1 : N);
   wf::Partial* part = static_cast<wf::Partial*>(workspace);
   if (wf::launch_sweep(logits, dtype, row_stride, total_rows, V, plan, part, stream) != hipSuccess)
     return WF_ERR_LAUNCH;
@@ -549,7 +549,7 @@ int32_t whiflash_verify_routed_entropy(const void* logits, int32_t dtype, int32_
   char* ws = static_cast<char*>(workspace);
   const size_t part_bytes = whiflash_verify_workspace_bytes(total_rows, V);
   const size_t best_bytes = round_up(static_cast<size_t>(B) * sizeof(int32_t), kWorkspaceAlign);
-  const wf::SweepPlan plan = wf::sweep_plan(total_rows, V);
+  const wf::SweepPlan plan = wf::few_rows_plan(total_rows, V, K + 1 > N ? K + 1 : N);
   wf::Partial* part = reinterpret_cast<wf::Partial*>(ws);
   int32_t* best = best_node ? best_node : reinterpret_cast<int32_t*>(ws + part_bytes);
   if (wf::launch_sweep(logits, dtype, row_stride, total_rows, V, plan, part, stream) != hipSuccess)

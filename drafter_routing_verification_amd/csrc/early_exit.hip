@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void early_exit_round_accept_kernel(
   const int32_t* dr = draft + static_cast<int64_t>(b) * K;
   const int draft0 = K > 0 ? chain_load(dr, K) : -1;
   FinishIn fin;
-  finish_load_pass<DT>(fin, zp, KS, B, m, b, 0, b1, W2);
+  finish_load_pass<DT>(fin, zp, KS, B, m, b, 0, b1, W2, b2, direct);
   MergeIn mi;
   merge_load(mi, part, splits, b * R, R);
   merge_finish(mi, part, splits, b * R, R, t_s, nullptr);
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void ee_round_prep_kernel(
   const int b = blockIdx.x;
   const HiddenSel direct{nullptr, nullptr, 0, 0};
   FinishIn fin;
-  finish_load_pass<DT>(fin, zp, KS, a.B, m, b, 0, b1, W2);
+  finish_load_pass<DT>(fin, zp, KS, a.B, m, b, 0, b1, W2, b2, direct);
   const float dal = router_finish_compute<DT>(fin, zp, direct, KS, a.B, m, b, b1, W2, b2, redf);
   const int c = dal > tau ? 1 : 0;
   if (threadIdx.x == 0) {

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kThreads) void round_finalize_kernel(
   RoutedIn in;
   routed_load_phase1(in, args, b);
   FinishIn fin;
-  finish_load_pass<DT>(fin, zp, KS, B, m, b, 0, b1, W2);
+  finish_load_pass<DT>(fin, zp, KS, B, m, b, 0, b1, W2, b2, direct);
   routed_load_phase2(in, args);
   const float dal = router_finish_compute<DT>(fin, zp, direct, KS, B, m, b, b1, W2, b2, redf);
   const int c = dal > tau ? 1 : 0;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void round_chain_finalize_kernel(
   const int32_t* dr = draft + static_cast<int64_t>(b) * K;
   const int draft0 = K > 0 ? chain_load(dr, K) : -1;
   FinishIn fin;
-  finish_load_pass<DT>(fin, zp, KS, B, m, b, 0, b1, W2);
+  finish_load_pass<DT>(fin, zp, KS, B, m, b, 0, b1, W2, b2, direct);
   MergeIn mi;
   merge_load(mi, part, splits, b * R, R);
   merge_finish(mi, part, splits, b * R, R, t_s, row_argmax);

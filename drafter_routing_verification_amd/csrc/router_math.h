@@ -30,12 +30,21 @@ constexpr int kFinishPer = 4;
 struct FinishIn {
   float part[kMaxRouterSlices][kFinishPer];
   float bias[kFinishPer], w2[kFinishPer];
+  float b2v;     // the second-layer bias (first pass only)
+  bool has_row;  // the sequence has a hidden row (first pass only)
 };
 
+// The first pass (base == 0) also loads b2 and the sequence's hidden-row
+// selection, so no load is left for after the reduction.
 template <int DT>
 __device__ inline void finish_load_pass(FinishIn& in, const float* __restrict__ zp, int KS, int B,
                                         int m, int b, int base, const float* __restrict__ b1,
-                                        const void* __restrict__ W2) {
+                                        const void* __restrict__ W2, const float* __restrict__ b2,
+                                        const HiddenSel& sel) {
+  if (base == 0) {
+    in.b2v = b2 ? *b2 : 0.f;
+    in.has_row = hidden_row(sel, b) >= 0;
+  }
   const int64_t slice_stride = static_cast<int64_t>(B) * m;
   const float* zb = zp + static_cast<int64_t>(b) * m;
 #pragma unroll
@@ -78,7 +87,7 @@ __device__ inline float router_finish_compute(const FinishIn& first, const float
   float acc = finish_fold_pass(first, KS, m, 0, 0.f);
   for (int base = kThreads * kFinishPer; base < m; base += kThreads * kFinishPer) {
     FinishIn in;
-    finish_load_pass<DT>(in, zp, KS, B, m, b, base, b1, W2);
+    finish_load_pass<DT>(in, zp, KS, B, m, b, base, b1, W2, b2, sel);
     acc = finish_fold_pass(in, KS, m, base, acc);
   }
 #pragma unroll
@@ -88,8 +97,8 @@ __device__ inline float router_finish_compute(const FinishIn& first, const float
   __syncthreads();
   float v = red[0];
   for (int w = 1; w < kWaves; ++w) v += red[w];
-  v += b2 ? *b2 : 0.f;
-  if (hidden_row(sel, b) < 0) v = NAN;  // no hidden row for this sequence
+  v += first.b2v;
+  if (!first.has_row) v = NAN;  // no hidden row for this sequence
   return v;
 }
 
@@ -100,7 +109,7 @@ __device__ inline float router_finish_sequence(const float* __restrict__ zp, con
                                                const void* __restrict__ W2,
                                                const float* __restrict__ b2, float* red) {
   FinishIn first;
-  finish_load_pass<DT>(first, zp, KS, B, m, b, 0, b1, W2);
+  finish_load_pass<DT>(first, zp, KS, B, m, b, 0, b1, W2, b2, sel);
   return router_finish_compute<DT>(first, zp, sel, KS, B, m, b, b1, W2, b2, red);
 }
 

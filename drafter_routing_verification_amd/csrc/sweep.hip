@@ -25,17 +25,24 @@ __device__ inline int xcd_contiguous_block() {
   return static_cast<int>(x * q + (x < r ? x : r) + k);
 }
 
-template <int DT>
+// Launches of at most kSmallLaunch workgroups fit in about two rounds of the
+// resident slots.  There few workgroups stream at once, so each thread issues
+// its whole batch of loads before comparing (sweep_chunk's kBatchTail form);
+// larger launches keep every slot busy with one load at a time per thread.
+constexpr int64_t kSmallLaunch = 4096;
+
+template <int DT, bool kBatch>
 __global__ __launch_bounds__(kSweepThreads) void argmax_sweep_kernel(
     const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
     int chunk_vecs, int nvec, Partial* __restrict__ part) {
-  sweep_chunk<DT, kSweepThreads>(xcd_contiguous_block(), logits, row_bytes, V, splits, chunk_vecs,
-                                 nvec, part);
+  sweep_chunk<DT, kSweepThreads, kBatch>(xcd_contiguous_block(), logits, row_bytes, V, splits,
+                                         chunk_vecs, nvec, part);
 }
 
 // The sweep's reads without its comparisons: the same chunks, workgroups,
 // numbering and loads, each thread folding its data into an XOR.  Workgroup
 // 0's XOR (chunk 0 of row 0) is written to *sink so the loads stay live.
+template <bool kBatch>
 __global__ __launch_bounds__(kSweepThreads) void stream_read_kernel(
     const unsigned char* __restrict__ logits, int64_t row_bytes, int splits, int chunk_vecs,
     int nvec, unsigned* __restrict__ sink) {
@@ -47,16 +54,28 @@ __global__ __launch_bounds__(kSweepThreads) void stream_read_kernel(
   const int v1 = min(v0 + chunk_vecs, nvec);
   unsigned acc = 0;
   int v = v0 + threadIdx.x;
-  for (; v + (kUnroll - 1) * kSweepThreads < v1; v += kUnroll * kSweepThreads) {
-    u32x4 d[kUnroll];
+  if constexpr (kBatch) {
+    for (; v < v1; v += kUnroll * kSweepThreads) {
+      u32x4 d[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) d[u] = load16(vp + v + u * kSweepThreads);
+      for (int u = 0; u < kUnroll; ++u)
+        if (v + u * kSweepThreads < v1) d[u] = load16(vp + v + u * kSweepThreads);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc ^= d[u][0] ^ d[u][1] ^ d[u][2] ^ d[u][3];
-  }
-  for (; v < v1; v += kSweepThreads) {
-    const u32x4 d = load16(vp + v);
-    acc ^= d[0] ^ d[1] ^ d[2] ^ d[3];
+      for (int u = 0; u < kUnroll; ++u)
+        if (v + u * kSweepThreads < v1) acc ^= d[u][0] ^ d[u][1] ^ d[u][2] ^ d[u][3];
+    }
+  } else {
+    for (; v + (kUnroll - 1) * kSweepThreads < v1; v += kUnroll * kSweepThreads) {
+      u32x4 d[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) d[u] = load16(vp + v + u * kSweepThreads);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc ^= d[u][0] ^ d[u][1] ^ d[u][2] ^ d[u][3];
+    }
+    for (; v < v1; v += kSweepThreads) {
+      const u32x4 d = load16(vp + v);
+      acc ^= d[0] ^ d[1] ^ d[2] ^ d[3];
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
@@ -117,16 +136,28 @@ hipError_t launch_sweep(const void* logits, int dtype, int64_t row_stride, int32
   const int64_t blocks = static_cast<int64_t>(rows) * plan.splits;
   if (blocks == 0) return hipSuccess;
   const unsigned char* base = static_cast<const unsigned char*>(logits);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kSweepThreads);
+  const bool small = blocks <= kSmallLaunch;
   if (dtype == WF_BF16) {
     using E = Elem<WF_BF16>;
-    hipLaunchKernelGGL(argmax_sweep_kernel<WF_BF16>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kSweepThreads), 0, stream, base, row_stride * E::kBytes, V, plan.splits,
-                       plan.chunk / E::kPerVec, V / E::kPerVec, part);
+    const int64_t rb = row_stride * E::kBytes;
+    const int cv = plan.chunk / E::kPerVec, nv = V / E::kPerVec;
+    if (small)
+      hipLaunchKernelGGL((argmax_sweep_kernel<WF_BF16, true>), grid, block, 0, stream, base, rb, V,
+                         plan.splits, cv, nv, part);
+    else
+      hipLaunchKernelGGL((argmax_sweep_kernel<WF_BF16, false>), grid, block, 0, stream, base, rb, V,
+                         plan.splits, cv, nv, part);
   } else {
     using E = Elem<WF_F32>;
-    hipLaunchKernelGGL(argmax_sweep_kernel<WF_F32>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kSweepThreads), 0, stream, base, row_stride * E::kBytes, V, plan.splits,
-                       plan.chunk / E::kPerVec, V / E::kPerVec, part);
+    const int64_t rb = row_stride * E::kBytes;
+    const int cv = plan.chunk / E::kPerVec, nv = V / E::kPerVec;
+    if (small)
+      hipLaunchKernelGGL((argmax_sweep_kernel<WF_F32, true>), grid, block, 0, stream, base, rb, V,
+                         plan.splits, cv, nv, part);
+    else
+      hipLaunchKernelGGL((argmax_sweep_kernel<WF_F32, false>), grid, block, 0, stream, base, rb, V,
+                         plan.splits, cv, nv, part);
   }
   return hipGetLastError();
 }
@@ -137,9 +168,14 @@ hipError_t launch_stream_read(const void* logits, int dtype, int64_t row_stride,
   if (blocks == 0) return hipSuccess;
   const int per = dtype == WF_BF16 ? Elem<WF_BF16>::kPerVec : Elem<WF_F32>::kPerVec;
   const int64_t bytes = dtype == WF_BF16 ? Elem<WF_BF16>::kBytes : Elem<WF_F32>::kBytes;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kSweepThreads),
-                     0, stream, static_cast<const unsigned char*>(logits), row_stride * bytes,
-                     plan.splits, plan.chunk / per, V / per, sink);
+  if (blocks <= kSmallLaunch)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kSweepThreads), 0, stream, static_cast<const unsigned char*>(logits),
+                       row_stride * bytes, plan.splits, plan.chunk / per, V / per, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kSweepThreads), 0, stream, static_cast<const unsigned char*>(logits),
+                       row_stride * bytes, plan.splits, plan.chunk / per, V / per, sink);
   return hipGetLastError();
 }
 
