@@ -47,28 +47,33 @@ __device__ inline void finish_load_pass(FinishIn& in, const float* __restrict__ 
   }
   const int64_t slice_stride = static_cast<int64_t>(B) * m;
   const float* zb = zp + static_cast<int64_t>(b) * m;
+  // Every load is issued unconditionally, from an index that is always valid
+  // (unit m - 1, slice KS - 1); finish_fold_pass drops what lies past m or KS.
+  // Guarded loads let the compiler sink each first use into the load's own
+  // branch, so every step of this loop waited for its load: four round trips
+  // instead of one.
 #pragma unroll
   for (int u = 0; u < kFinishPer; ++u) {
     const int j = base + u * kThreads + threadIdx.x;
-    const bool ok = j < m;
+    const int jc = j < m ? j : m - 1;
 #pragma unroll
     for (int s = 0; s < kMaxRouterSlices; ++s)
-      in.part[s][u] = (ok && s < KS) ? zb[s * slice_stride + j] : 0.f;
-    in.bias[u] = (ok && b1) ? b1[j] : 0.f;
-    in.w2[u] = ok ? load_elem<DT>(W2, j) : 0.f;
+      in.part[s][u] = zb[(s < KS ? s : KS - 1) * slice_stride + jc];
+    in.bias[u] = b1 ? b1[jc] : 0.f;
+    in.w2[u] = load_elem<DT>(W2, jc);
   }
 }
 
+// Units past m (their loads repeated unit m - 1) and slices past KS are
+// dropped here, by selects on loaded values.
 __device__ inline float finish_fold_pass(const FinishIn& in, int KS, int m, int base, float acc) {
 #pragma unroll
   for (int u = 0; u < kFinishPer; ++u) {
-    if (base + u * kThreads + static_cast<int>(threadIdx.x) < m) {
-      float z = 0.f;
+    float z = 0.f;
 #pragma unroll
-      for (int s = 0; s < kMaxRouterSlices; ++s)
-        if (s < KS) z += in.part[s][u];
-      acc += in.w2[u] * gelu(z + in.bias[u]);
-    }
+    for (int s = 0; s < kMaxRouterSlices; ++s) z += s < KS ? in.part[s][u] : 0.f;
+    const float c = in.w2[u] * gelu(z + in.bias[u]);
+    acc += base + u * kThreads + static_cast<int>(threadIdx.x) < m ? c : 0.f;
   }
   return acc;
 }
