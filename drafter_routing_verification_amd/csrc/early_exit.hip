@@ -304,11 +304,13 @@ __device__ void ee_tree_read(const EeTreeArgs& a, int splits, int chunk_vecs, in
   __shared__ float bv_s;
   __shared__ int bi_s;
   const int tid = threadIdx.x;
-  // Edges of this sequence (one per node), consumed after the sweep.
+  // Edges of this sequence (one per node), consumed after the sweep.  They are
+  // loaded unconditionally (threads past Rmax read the last node's edge and
+  // ignore it): guarded loads let the compiler test each edge as soon as it
+  // arrived, which held the sweep back by two round trips.
   const int4* eb = a.edge + static_cast<int64_t>(b) * a.Rmax;
-  const int4 none = make_int4(-1, -1, 0, 0);
-  const int4 e0 = tid < a.Rmax ? eb[tid] : none;
-  const int4 e1 = tid + kEeThreads < a.Rmax ? eb[tid + kEeThreads] : none;
+  const int4 e0 = eb[tid < a.Rmax ? tid : a.Rmax - 1];
+  const int4 e1 = eb[tid + kEeThreads < a.Rmax ? tid + kEeThreads : a.Rmax - 1];
   const Partial r = sweep_chunk<DT, kEeThreads, true>(row * splits + c, a.logits, a.row_bytes, a.V,
                                                       splits, chunk_vecs, nvec, part);
   if (tid == 0) {
@@ -321,13 +323,13 @@ __device__ void ee_tree_read(const EeTreeArgs& a, int splits, int chunk_vecs, in
   unsigned long long* mb = a.mask + static_cast<int64_t>(b) * a.W;
   // A child whose (logit, token) is beaten inside this chunk is not the greedy
   // token of this row, so it is not accepted.
-  if (e0.w && e0.x == u) {
+  if (tid < a.Rmax && e0.w && e0.x == u) {
     const float xv = __int_as_float(e0.z);
     if (bv > xv || (bv == xv && bi < e0.y))
       __hip_atomic_fetch_or(&mb[tid >> 6], 1ull << (tid & 63), __ATOMIC_RELAXED,
                             __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (e1.w && e1.x == u) {
+  if (tid + kEeThreads < a.Rmax && e1.w && e1.x == u) {
     const int v = tid + kEeThreads;
     const float xv = __int_as_float(e1.z);
     if (bv > xv || (bv == xv && bi < e1.y))
@@ -343,18 +345,21 @@ __device__ void ee_tree_group(const EeTreeArgs& a, int splits, int chunk_vecs, i
                               Partial* __restrict__ part, int u, int b0, int nb, int c) {
   __shared__ int grow_s[kTreeGroup];
   __shared__ int grej_s[kTreeGroup];
+  static_assert(kTreeGroup * kMaxMaskWords <= kEeThreads, "one (sequence, mask word) per thread");
   const int tid = threadIdx.x;
+  // Every item's row and mask words in one round of loads, issued
+  // unconditionally (threads past the items read item 0 and ignore it).
+  const int nw = nb * a.W;
+  const int t = tid < nw ? tid : 0;
+  const int j = t / a.W, w = t - j * a.W;
+  const int row = a.rowmap[static_cast<int64_t>(u) * a.B + b0 + (tid < nb ? tid : 0)];
+  const unsigned long long m = __hip_atomic_load(&a.mask[static_cast<int64_t>(b0 + j) * a.W + w],
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long an = a.anc[(static_cast<int64_t>(b0 + j) * a.Rmax + u) * a.W + w];
   if (tid < kTreeGroup) grej_s[tid] = 0;
   __syncthreads();
-  if (tid < nb) grow_s[tid] = a.rowmap[static_cast<int64_t>(u) * a.B + b0 + tid];
-  for (int t = tid; t < nb * a.W; t += kEeThreads) {
-    const int j = t / a.W, w = t - j * a.W;
-    const int b = b0 + j;
-    const unsigned long long m = __hip_atomic_load(&a.mask[static_cast<int64_t>(b) * a.W + w],
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long an = a.anc[(static_cast<int64_t>(b) * a.Rmax + u) * a.W + w];
-    if ((m & an) != 0ull) grej_s[j] = 1;
-  }
+  if (tid < nb) grow_s[tid] = row;
+  if (tid < nw && (m & an) != 0ull) grej_s[j] = 1;
   __syncthreads();
   for (int j = 0; j < nb; ++j) {
     const int row = grow_s[j];
@@ -389,14 +394,14 @@ __global__ __launch_bounds__(kEeThreads) void ee_tree_sweep_kernel(EeTreeArgs a,
   __shared__ int row_s;
   const int tid = threadIdx.x;
   if (tid < 64) {
-    const int row = tid == 0 ? a.rowmap[static_cast<int64_t>(u) * a.B + b] : 0;
-    bool hit = false;
-    if (tid < a.W) {
-      const unsigned long long m = __hip_atomic_load(&a.mask[static_cast<int64_t>(b) * a.W + tid],
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const unsigned long long an = a.anc[(static_cast<int64_t>(b) * a.Rmax + u) * a.W + tid];
-      hit = (m & an) != 0ull;
-    }
+    // The row and the mask words are loaded together, unconditionally (lanes
+    // past W read word 0 and ignore it), in one round trip.
+    const int row = a.rowmap[static_cast<int64_t>(u) * a.B + b];
+    const int w = tid < a.W ? tid : 0;
+    const unsigned long long m = __hip_atomic_load(&a.mask[static_cast<int64_t>(b) * a.W + w],
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long an = a.anc[(static_cast<int64_t>(b) * a.Rmax + u) * a.W + w];
+    const bool hit = tid < a.W && (m & an) != 0ull;
     const bool rejected = __ballot(hit) != 0ull;
     if (tid == 0) row_s = rejected ? -1 : row;
   }
