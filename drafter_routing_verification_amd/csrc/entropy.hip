@@ -17,7 +17,7 @@
 namespace wf {
 namespace {
 
-constexpr int kEntUnroll = 4;
+constexpr int kEntUnroll = 8;  // 16-byte loads in flight per thread
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void entropy_partial_kernel(
@@ -43,15 +43,18 @@ __global__ __launch_bounds__(kThreads) void entropy_partial_kernel(
 #pragma unroll
       for (int k = 0; k < E::kPerVec; ++k) ent_add(acc, E::at(d, k), mb);
     };
-    int v = v0 + tid;
-    for (; v + (kEntUnroll - 1) * kThreads < v1; v += kEntUnroll * kThreads) {
+    // Each thread issues its whole batch of loads (missing ones masked off)
+    // before absorbing any: one round trip per batch for the few workgroups
+    // of this pass.
+    for (int v = v0 + tid; v < v1; v += kEntUnroll * kThreads) {
       u32x4 d[kEntUnroll];
 #pragma unroll
-      for (int u = 0; u < kEntUnroll; ++u) d[u] = load16(vp + v + u * kThreads);
+      for (int u = 0; u < kEntUnroll; ++u)
+        if (v + u * kThreads < v1) d[u] = load16(vp + v + u * kThreads);
 #pragma unroll
-      for (int u = 0; u < kEntUnroll; ++u) absorb(d[u]);
+      for (int u = 0; u < kEntUnroll; ++u)
+        if (v + u * kThreads < v1) absorb(d[u]);
     }
-    for (; v < v1; v += kThreads) absorb(load16(vp + v));
     if (c == splits - 1 && tid == 0) {
       for (int e = nvec * E::kPerVec; e < V; ++e) {
         const float x = E::scalar(rowp, e);
