@@ -14,18 +14,21 @@ __global__ __launch_bounds__(kThreads) void catchup_kernel(
     int32_t* __restrict__ catchup_len) {
   const int b = blockIdx.x * kThreads + threadIdx.x;
   if (b >= B) return;
+  // Both backlog entries are loaded with the inputs, in one round trip, and
+  // updated without branches; a sequence with an out-of-range choice gets its
+  // entries written back unchanged.
+  int32_t* bl = backlog + 2 * static_cast<int64_t>(b);
   const int c = cur[b], n = nxt[b], a = accept_len[b];
-  int sw = 0, cu = 0;
-  if ((c == 0 || c == 1) && (n == 0 || n == 1)) {
-    int32_t* bl = backlog + 2 * static_cast<int64_t>(b);
-    if (a > 0) bl[1 - c] += a;
-    if (n != c) {
-      sw = 1;
-      cu = bl[n];
-      bl[n] = 0;
-    }
-  }
-  if (switch_flag) switch_flag[b] = sw;
+  const int x0 = bl[0], x1 = bl[1];
+  const bool ok = (c == 0 || c == 1) && (n == 0 || n == 1);
+  const int add = ok && a > 0 ? a : 0;
+  const int y0 = x0 + (c == 1 ? add : 0);  // tokens accepted while drafter 0 was idle
+  const int y1 = x1 + (c == 0 ? add : 0);
+  const bool sw = ok && n != c;
+  const int cu = sw ? (n == 0 ? y0 : y1) : 0;
+  bl[0] = sw && n == 0 ? 0 : y0;
+  bl[1] = sw && n == 1 ? 0 : y1;
+  if (switch_flag) switch_flag[b] = sw ? 1 : 0;
   if (catchup_len) catchup_len[b] = cu;
 }
 
