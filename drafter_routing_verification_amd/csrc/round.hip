@@ -76,8 +76,8 @@ __global__ __launch_bounds__(kThreads) void round_chain_finalize_kernel(
 }
 
 // First launch of a small-batch round: workgroups [0, router_blocks) run the
-// router's GEMV tiles (workgroup i: hidden units 4 (i % router_gx) .. + 3 for
-// every sequence, all B <= NB of them), the rest run the argmax sweep's chunks.
+// router's GEMV tiles (workgroup i: hidden units 4 i .. 4 i + 3 for every
+// sequence, all B <= NB of them), the rest run the argmax sweep's chunks.
 // The two halves read disjoint inputs and write disjoint outputs.  At a few
 // sequences both are small and latency-bound, so one launch instead of two
 // saves a launch floor; at large batches the router runs on MFMA tiles in a
@@ -85,13 +85,12 @@ __global__ __launch_bounds__(kThreads) void round_chain_finalize_kernel(
 template <int DTL, int DTH, int NB>
 __global__ __launch_bounds__(kThreads) void router_sweep_kernel(
     const void* __restrict__ hidden, int B, int d, const void* __restrict__ W1, int m,
-    float* __restrict__ zp, int router_gx, int router_blocks,
-    const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
-    int chunk_vecs, int nvec, Partial* __restrict__ part) {
+    float* __restrict__ zp, int router_blocks, const unsigned char* __restrict__ logits,
+    int64_t row_bytes, int V, int splits, int chunk_vecs, int nvec, Partial* __restrict__ part) {
   const int i = blockIdx.x;
   if (i < router_blocks) {
     const HiddenSel direct{nullptr, nullptr, 0, 0};
-    gemv_tile<DTH, NB, true>(i % router_gx, 0, hidden, direct, B, d, W1, m, zp);
+    gemv_tile<DTH, NB, true>(i, 0, hidden, direct, B, d, W1, m, zp);
   } else {
     // Few rows, few workgroups per CU: each thread issues its whole batch of loads at once.
     sweep_chunk<DTL, kThreads, true>(i - router_blocks, logits, row_bytes, V, splits, chunk_vecs,
@@ -101,14 +100,14 @@ __global__ __launch_bounds__(kThreads) void router_sweep_kernel(
 
 template <int DTL, int DTH>
 hipError_t launch_router_sweep_nb(unsigned grid, int nb, const void* hidden, int B, int d,
-                                  const void* W1, int m, float* zp, int router_gx,
-                                  int router_blocks, const unsigned char* logits,
-                                  int64_t row_bytes, int V, int splits, int chunk_vecs, int nvec,
-                                  Partial* part, hipStream_t stream) {
+                                  const void* W1, int m, float* zp, int router_blocks,
+                                  const unsigned char* logits, int64_t row_bytes, int V,
+                                  int splits, int chunk_vecs, int nvec, Partial* part,
+                                  hipStream_t stream) {
 #define WF_ROUTER_SWEEP(NBV)                                                                   \
   hipLaunchKernelGGL((router_sweep_kernel<DTL, DTH, NBV>), dim3(grid), dim3(kThreads), 0, stream, \
-                     hidden, B, d, W1, m, zp, router_gx, router_blocks, logits, row_bytes, V,   \
-                     splits, chunk_vecs, nvec, part)
+                     hidden, B, d, W1, m, zp, router_blocks, logits, row_bytes, V, splits,      \
+                     chunk_vecs, nvec, part)
   if (nb == 1) WF_ROUTER_SWEEP(1);
   else if (nb == 2) WF_ROUTER_SWEEP(2);
   else if (nb == 4) WF_ROUTER_SWEEP(4);
@@ -168,18 +167,18 @@ hipError_t launch_round_stage1(bool fused, const RouterPlan& plan, int hidden_dt
     const int64_t rb = row_stride * E::kBytes;
     const int cv = sp.chunk / E::kPerVec, nv = V / E::kPerVec;
     return hidden_dtype == WF_BF16
-               ? launch_router_sweep_nb<WF_BF16, WF_BF16>(grid, nb, hidden, B, d, W1, m, zp, gx, gx,
+               ? launch_router_sweep_nb<WF_BF16, WF_BF16>(grid, nb, hidden, B, d, W1, m, zp, gx,
                                                           base, rb, V, sp.splits, cv, nv, part, stream)
-               : launch_router_sweep_nb<WF_BF16, WF_F32>(grid, nb, hidden, B, d, W1, m, zp, gx, gx,
+               : launch_router_sweep_nb<WF_BF16, WF_F32>(grid, nb, hidden, B, d, W1, m, zp, gx,
                                                          base, rb, V, sp.splits, cv, nv, part, stream);
   }
   using E = Elem<WF_F32>;
   const int64_t rb = row_stride * E::kBytes;
   const int cv = sp.chunk / E::kPerVec, nv = V / E::kPerVec;
   return hidden_dtype == WF_BF16
-             ? launch_router_sweep_nb<WF_F32, WF_BF16>(grid, nb, hidden, B, d, W1, m, zp, gx, gx,
+             ? launch_router_sweep_nb<WF_F32, WF_BF16>(grid, nb, hidden, B, d, W1, m, zp, gx,
                                                        base, rb, V, sp.splits, cv, nv, part, stream)
-             : launch_router_sweep_nb<WF_F32, WF_F32>(grid, nb, hidden, B, d, W1, m, zp, gx, gx,
+             : launch_router_sweep_nb<WF_F32, WF_F32>(grid, nb, hidden, B, d, W1, m, zp, gx,
                                                       base, rb, V, sp.splits, cv, nv, part, stream);
 }
 
