@@ -7,7 +7,7 @@
 #define WF_SWEEP_THREADS 256
 #endif
 #ifndef WF_SWEEP_CHUNK
-#define WF_SWEEP_CHUNK 12800
+#define WF_SWEEP_CHUNK 14400
 #endif
 
 namespace wf {
@@ -92,11 +92,16 @@ __global__ __launch_bounds__(kSweepThreads) void stream_read_kernel(
 }  // namespace
 
 SweepPlan sweep_plan(int32_t rows, int32_t V) {
-  // 256-thread workgroups over chunks of ~12.8K elements (~25 KB of bf16),
+  // 256-thread workgroups over chunks of ~14.4K elements (~28 KB of bf16),
   // rounded down to an odd count per row: 11 per 151,936-wide row (13,824
-  // elements) and 11 per 128,256-wide row.  Small batches split further so a
-  // launch still has about 2048 workgroups, but never below 2048 elements per
-  // chunk.
+  // elements) and 9 per 128,256-wide row (14,336).  Small batches split
+  // further so a launch still has about 2048 workgroups, but never below 2048
+  // elements per chunk.
+  //
+  // Same-box A/B on the Llama-shape chain workload (2,816 x 128,256 rows, three
+  // interleaved trials): 9 chunks per row (this target) 104.96-105.31 us for
+  // the sweep, 11 chunks (a 12.8K target) 105.83-106.37 us.  The 151,936-wide
+  // rows get 11 chunks either way.
   //
   // Same-process A/B, whole verify call, on the routed / chain / Llama-shape
   // chain workloads (4,992 x 151,936, 4,352 x 151,936 and 2,816 x 128,256
