@@ -91,7 +91,8 @@ def _sweep_source_hash() -> str:
 
 
 def _traffic(workload: str, launches_bytes: float):
-    """HBM bytes per sweep launch from the committed counter summary, if the kernel is unchanged."""
+    """HBM bytes per launch of the sweep kernel alone (the unit `achieved` is timed on), from
+    the committed counter summary, if the kernel is unchanged."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -100,7 +101,7 @@ def _traffic(workload: str, launches_bytes: float):
     entry = rec.get(workload)
     if not entry or entry.get("sweep_source_sha256_16") != _sweep_source_hash():
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry.get("sweep_kernel_hbm_bytes_per_launch")
 
 
 # ----------------------------------------------------------------------------- CPU oracle baseline
