@@ -10,7 +10,8 @@
 //     are issued up front as row-contiguous 16-byte loads, staged chunk by
 //     chunk through LDS, and multiplied with v_mfma_f32_16x16x32_bf16 (float32
 //     accumulate).  Splitting the hidden size across workgroups keeps every CU
-//     busy while each moves ~120 KB instead of ~300 KB.
+//     busy: at 256 sequences of 2560 -> 1024, two slices give 256 workgroups
+//     of 96 rows x 1280 columns (240 KiB of operands each, not 480 KiB).
 // Stage 2, router_finish_kernel, one workgroup per sequence: sums the KS
 // partials, adds b1, applies GELU and W2, sums over j and adds b2, all in
 // float32 and in a fixed order (bitwise reproducible), then thresholds.
