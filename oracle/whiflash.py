@@ -37,7 +37,8 @@ def decode_logits(raw: np.ndarray, dtype: str) -> np.ndarray:
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         bits = np.asarray(raw, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-        return bits.view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):  # NaN patterns widen to NaN, as they should
+            return bits.view(np.float32).astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
