@@ -163,7 +163,7 @@ int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int3
                               int64_t row_stride, const int32_t* draft, int32_t* accept_len,
                               int32_t* bonus, int32_t* row_argmax, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
-  if (B < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
+  if (B < 0 || K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
   const int64_t rows64 = static_cast<int64_t>(B) * (K + 1);
   if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
   const int32_t rows = static_cast<int32_t>(rows64);
@@ -183,11 +183,12 @@ int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int3
 
 size_t whiflash_early_exit_workspace_bytes(int32_t B, int32_t K, int32_t V) {
   if (B <= 0 || K < 0 || V <= 0) return 0;
+  const int64_t rows = static_cast<int64_t>(B) * (static_cast<int64_t>(K) + 1);
+  if (rows > INT32_MAX) return 0;  // more rows than the call accepts
   const wf::SweepPlan plan = wf::early_exit_plan(B, V);
   // Per-sequence mismatch flags, then the chunk partials of every row.
   return round_up(static_cast<size_t>(B) * sizeof(int32_t), kWorkspaceAlign) +
-         round_up(static_cast<size_t>(B) * (K + 1) * plan.splits * sizeof(wf::Partial),
-                  kWorkspaceAlign);
+         round_up(static_cast<size_t>(rows) * plan.splits * sizeof(wf::Partial), kWorkspaceAlign);
 }
 
 int32_t whiflash_verify_chain_early_exit(const void* logits, int32_t dtype, int32_t B, int32_t K,
@@ -195,7 +196,7 @@ int32_t whiflash_verify_chain_early_exit(const void* logits, int32_t dtype, int3
                                          int32_t* accept_len, int32_t* bonus, int32_t* row_argmax,
                                          void* workspace, size_t workspace_bytes,
                                          hipStream_t stream) {
-  if (B < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
+  if (B < 0 || K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
   const int64_t rows64 = static_cast<int64_t>(B) * (K + 1);
   if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
   const int32_t rows = static_cast<int32_t>(rows64);
@@ -246,7 +247,7 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
                                const int32_t* d2t, int32_t Vd, int32_t* accept_len, int32_t* bonus,
                                int32_t* best_node, int32_t* row_argmax, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-  if (B < 0 || total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+  if (B < 0 || total_rows < 0 || K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
       N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
     return WF_ERR_SHAPE;
   int32_t s = check_logits(logits, dtype, total_rows, V, row_stride);
@@ -269,12 +270,15 @@ int32_t whiflash_verify_routed(const void* logits, int32_t dtype, int32_t B, int
 
 size_t whiflash_tree_early_exit_workspace_bytes(int32_t B, int32_t N, int32_t V) {
   if (B <= 0 || N <= 0 || N > WHIFLASH_MAX_SEQ_ROWS || V <= 0) return 0;
-  return wf::ee_tree_workspace(B, N, B * N, V, kWorkspaceAlign).total;
+  const int64_t rows = static_cast<int64_t>(B) * N;
+  if (rows > INT32_MAX) return 0;  // more rows than the call accepts
+  return wf::ee_tree_workspace(B, N, static_cast<int32_t>(rows), V, kWorkspaceAlign).total;
 }
 
 size_t whiflash_routed_early_exit_workspace_bytes(int32_t B, int32_t K, int32_t N, int32_t total_rows,
                                                   int32_t V) {
   if (B <= 0 || K < 0 || N <= 0 || total_rows < 0 || V <= 0) return 0;
+  if (K >= WHIFLASH_MAX_SEQ_ROWS) return 0;
   const int32_t rmax = K + 1 > N ? K + 1 : N;
   if (rmax > WHIFLASH_MAX_SEQ_ROWS) return 0;
   return wf::ee_tree_workspace(B, rmax, total_rows, V, kWorkspaceAlign).total;
@@ -299,7 +303,7 @@ int32_t whiflash_round_routed(const void* hidden, int32_t hidden_dtype, int32_t 
   if (!valid_dtype(hidden_dtype)) return WF_ERR_DTYPE;
   if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
   // Verify arguments, as whiflash_verify_routed.
-  if (total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+  if (total_rows < 0 || K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
       N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
     return WF_ERR_SHAPE;
   int32_t s = check_logits(logits, logits_dtype, total_rows, V, row_stride);
@@ -452,7 +456,7 @@ int32_t whiflash_verify_routed_early_exit(const void* logits, int32_t dtype, int
                                           int32_t* bonus, int32_t* best_node, int32_t* row_argmax,
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream) {
-  if (B < 0 || total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+  if (B < 0 || total_rows < 0 || K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
       N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
     return WF_ERR_SHAPE;
   int32_t s = check_logits(logits, dtype, total_rows, V, row_stride);
@@ -482,7 +486,7 @@ int32_t whiflash_round_routed_early_exit(
     size_t workspace_bytes, hipStream_t stream) {
   if (!valid_dtype(hidden_dtype)) return WF_ERR_DTYPE;
   if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
-  if (total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+  if (total_rows < 0 || K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
       N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
     return WF_ERR_SHAPE;
   int32_t s = check_logits(logits, logits_dtype, total_rows, V, row_stride);
@@ -532,7 +536,7 @@ int32_t whiflash_verify_routed_entropy(const void* logits, int32_t dtype, int32_
                                        int32_t* row_argmax, float* entropy, int32_t* next_choice,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream) {
-  if (B < 0 || total_rows < 0 || K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
+  if (B < 0 || total_rows < 0 || K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS || N < 1 ||
       N > WHIFLASH_MAX_SEQ_ROWS || Vd < 1)
     return WF_ERR_SHAPE;
   int32_t s = check_logits(logits, dtype, total_rows, V, row_stride);
@@ -566,8 +570,10 @@ int32_t whiflash_verify_routed_entropy(const void* logits, int32_t dtype, int32_
 
 size_t whiflash_round_chain_workspace_bytes(int32_t B, int32_t m, int32_t K, int32_t V) {
   if (B <= 0 || m <= 0 || K < 0 || V <= 0) return 0;
+  const int64_t rows = static_cast<int64_t>(B) * (static_cast<int64_t>(K) + 1);
+  if (rows > INT32_MAX) return 0;  // more rows than the call accepts
   return whiflash_route_workspace_bytes(B, m) +
-         whiflash_verify_workspace_bytes(static_cast<int32_t>(static_cast<int64_t>(B) * (K + 1)), V);
+         whiflash_verify_workspace_bytes(static_cast<int32_t>(rows), V);
 }
 
 int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
@@ -581,7 +587,7 @@ int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d
   if (!valid_dtype(hidden_dtype)) return WF_ERR_DTYPE;
   if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
   // Verify arguments, as whiflash_verify_chain.
-  if (K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
+  if (K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
   const int64_t rows64 = static_cast<int64_t>(B) * (K + 1);
   if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
   const int32_t rows = static_cast<int32_t>(rows64);
@@ -614,7 +620,8 @@ int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d
 size_t whiflash_round_chain_early_exit_workspace_bytes(int32_t B, int32_t m, int32_t K,
                                                        int32_t V) {
   if (B <= 0 || m <= 0 || K < 0 || V <= 0) return 0;
-  return whiflash_route_workspace_bytes(B, m) + whiflash_early_exit_workspace_bytes(B, K, V);
+  const size_t ee = whiflash_early_exit_workspace_bytes(B, K, V);
+  return ee == 0 ? 0 : whiflash_route_workspace_bytes(B, m) + ee;
 }
 
 int32_t whiflash_round_chain_early_exit(const void* hidden, int32_t hidden_dtype, int32_t d,
@@ -627,7 +634,7 @@ int32_t whiflash_round_chain_early_exit(const void* hidden, int32_t hidden_dtype
                                         size_t workspace_bytes, hipStream_t stream) {
   if (!valid_dtype(hidden_dtype)) return WF_ERR_DTYPE;
   if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
-  if (K < 0 || K + 1 > WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
+  if (K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
   const int64_t rows64 = static_cast<int64_t>(B) * (K + 1);
   if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
   int32_t s = check_logits(logits, logits_dtype, static_cast<int32_t>(rows64), V, row_stride);

@@ -176,7 +176,7 @@ int32_t whiflash_verify_chain(const void* logits, int32_t dtype, int32_t B, int3
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes whiflash_verify_chain_early_exit needs (host-only; 0 when
- * B <= 0, K < 0 or V <= 0). */
+ * B <= 0, K < 0, V <= 0 or B * (K + 1) exceeds INT32_MAX). */
 size_t whiflash_early_exit_workspace_bytes(int32_t B, int32_t K, int32_t V);
 
 /*

@@ -228,3 +228,20 @@ def test_stream_read_validation():
     assert f(ALIGNED, 5, 4352, V, V, ALIGNED, None) == -3
     assert f(ALIGNED, 1, 4352, V, V - 8, ALIGNED, None) == -2
     assert f(ALIGNED + 8, 1, 4352, V, V, ALIGNED, None) == -4
+
+
+def test_workspace_queries_reject_row_counts_past_int32():
+    # Sizes whose row count B*(K+1) or B*N exceeds INT32_MAX are rejected by the
+    # calls, and their workspace queries answer 0 rather than overflow.
+    big = 2**31 - 1
+    assert wf.early_exit_workspace_bytes(2**21, 1023, V) == 0
+    assert wf.early_exit_workspace_bytes(2, big, V) == 0
+    assert wf.round_chain_workspace_bytes(2**21, 1024, 1023, V) == 0
+    assert wf.round_chain_workspace_bytes(2, 1024, big, V) == 0
+    assert wf.round_chain_early_exit_workspace_bytes(2**21, 1024, 1023, V) == 0
+    assert wf.tree_early_exit_workspace_bytes(2**22, 1024, V) == 0
+    assert wf.routed_early_exit_workspace_bytes(4, big, 16, 64, V) == 0
+    assert wf.round_early_exit_workspace_bytes(4, 1024, big, 16, 64, V) == 0
+    # Just inside the limit the queries still answer.
+    assert wf.early_exit_workspace_bytes(2**21 - 1, 1023, V) > 0
+    assert wf.tree_early_exit_workspace_bytes(2**21 - 1, 1024, V) > 0
