@@ -259,7 +259,7 @@ def _stream(t: torch.Tensor, stream) -> int:
 
 
 def _device_tensor(t: torch.Tensor, name: str) -> None:
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a GPU tensor")
 
 
@@ -273,13 +273,76 @@ def _i32(t: torch.Tensor, name: str, numel: int | None = None) -> torch.Tensor:
 
 
 def _workspace(ws, nbytes: int, device) -> torch.Tensor | None:
-    if nbytes == 0:
-        return ws
     if ws is None:
-        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+    _device_tensor(ws, "workspace")
+    if ws.get_device() != device.index or not ws.is_contiguous():
+        raise TypeError(f"workspace must be a contiguous tensor on {device}")
     if ws.numel() * ws.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
     return ws
+
+
+def _out(t, dtype: torch.dtype, numel: int, device, name: str) -> torch.Tensor:
+    """A caller-supplied output tensor, checked (the kernels write `numel` elements of
+    `dtype` through its pointer), or a new one when t is None."""
+    if t is None:
+        return torch.empty(numel, dtype=dtype, device=device)
+    _device_tensor(t, name)
+    if t.get_device() != device.index or t.dtype != dtype or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {dtype} tensor on {device}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} must hold at least {numel} elements, has {t.numel()}")
+    return t
+
+
+def _opt_out(t, numel: int, device, name: str) -> torch.Tensor | None:
+    """An optional int32 output: True allocates it, False or None skips it, a tensor is checked."""
+    if t is True:
+        return torch.empty(max(numel, 1), dtype=torch.int32, device=device)
+    if t is False or t is None:
+        return None
+    return _out(t, torch.int32, numel, device, name)
+
+
+def _on(device, **tensors) -> None:
+    """Every given tensor (None skipped) lives on `device`: the kernels dereference them there."""
+    idx = device.index
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        _device_tensor(t, name)
+        if t.get_device() != idx:
+            raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+
+
+def _weights(hidden: torch.Tensor, hidden_name: str, W1, W2) -> None:
+    """The hidden states and both router weights: contiguous GPU tensors of one dtype on
+    the device of the hidden states."""
+    _device_tensor(hidden, hidden_name)
+    idx, dt = hidden.get_device(), hidden.dtype
+    for t, name in ((hidden, hidden_name), (W1, "W1"), (W2, "W2")):
+        _device_tensor(t, name)
+        if not t.is_contiguous() or t.dtype != dt:
+            raise TypeError(f"{name} must be contiguous with the dtype of {hidden_name}")
+        if t.get_device() != idx:
+            raise ValueError(f"{name} is on {t.device}, {hidden_name} on {hidden.device}")
+
+
+def _biases(b1, b2, m: int, device):
+    """b1: None or a contiguous float32 tensor of m elements; b2: None, a float, or a
+    1-element float32 tensor.  Returns (b1, b2) with b2 as a device tensor or None."""
+    if b1 is not None:
+        _on(device, b1=b1)
+        if b1.dtype != torch.float32 or b1.numel() != m or not b1.is_contiguous():
+            raise TypeError("b1 must be a contiguous float32 tensor of m elements")
+    if b2 is not None and not isinstance(b2, torch.Tensor):
+        b2 = torch.tensor([float(b2)], dtype=torch.float32, device=device)
+    if b2 is not None:
+        _on(device, b2=b2)
+        if b2.dtype != torch.float32 or b2.numel() != 1:
+            raise TypeError("b2 must be a float or a 1-element float32 tensor")
+    return b1, b2
 
 
 def _rows_view(logits: torch.Tensor, rows: int) -> tuple[int, int]:
@@ -311,21 +374,13 @@ def route(hidden, W1, b1, W2, b2, tau: float, *, delta_al=None, choice=None, wor
     _device_tensor(hidden, "hidden")
     B, d = hidden.shape
     m = W1.shape[0]
-    for t, name in ((hidden, "hidden"), (W1, "W1"), (W2, "W2")):
-        _device_tensor(t, name)
-        if not t.is_contiguous() or t.dtype != hidden.dtype:
-            raise TypeError(f"{name} must be contiguous with the dtype of hidden")
+    _weights(hidden, "hidden", W1, W2)
     if tuple(W1.shape) != (m, d) or W2.numel() != m:
         raise ValueError("W1 must be [m, d] and W2 hold m elements")
     dev = hidden.device
-    if b1 is not None and (b1.dtype != torch.float32 or b1.numel() != m or not b1.is_contiguous()):
-        raise TypeError("b1 must be a contiguous float32 tensor of m elements")
-    if b2 is not None and not isinstance(b2, torch.Tensor):
-        b2 = torch.tensor([float(b2)], dtype=torch.float32, device=dev)
-    if delta_al is None:
-        delta_al = torch.empty(B, dtype=torch.float32, device=dev)
-    if choice is None:
-        choice = torch.empty(B, dtype=torch.int32, device=dev)
+    b1, b2 = _biases(b1, b2, m, dev)
+    delta_al = _out(delta_al, torch.float32, B, dev, "delta_al")
+    choice = _out(choice, torch.int32, B, dev, "choice")
     ws = _workspace(workspace, route_workspace_bytes(B, m), dev)
     _check(whiflash_route(_ptr(hidden), _dtype_code(hidden), B, d, _ptr(W1), _ptr(b1), m, _ptr(W2),
                           _ptr(b2), float(tau), _ptr(delta_al), _ptr(choice), _ptr(ws),
@@ -342,10 +397,7 @@ def route_gather(hidden_rows, pos, W1, b1, W2, b2, tau: float, *, row0=None, row
     total_rows, d = hidden_rows.shape
     B = pos.numel()
     m = W1.shape[0]
-    for t, name in ((hidden_rows, "hidden_rows"), (W1, "W1"), (W2, "W2")):
-        _device_tensor(t, name)
-        if not t.is_contiguous() or t.dtype != hidden_rows.dtype:
-            raise TypeError(f"{name} must be contiguous with the dtype of hidden_rows")
+    _weights(hidden_rows, "hidden_rows", W1, W2)
     if tuple(W1.shape) != (m, d) or W2.numel() != m:
         raise ValueError("W1 must be [m, d] and W2 hold m elements")
     _i32(pos, "pos", B)
@@ -354,12 +406,10 @@ def route_gather(hidden_rows, pos, W1, b1, W2, b2, tau: float, *, row0=None, row
         if row0.numel() < B:
             raise ValueError("row0 must hold at least B entries")
     dev = hidden_rows.device
-    if b1 is not None and (b1.dtype != torch.float32 or b1.numel() != m or not b1.is_contiguous()):
-        raise TypeError("b1 must be a contiguous float32 tensor of m elements")
-    if b2 is not None and not isinstance(b2, torch.Tensor):
-        b2 = torch.tensor([float(b2)], dtype=torch.float32, device=dev)
-    delta_al = torch.empty(B, dtype=torch.float32, device=dev) if delta_al is None else delta_al
-    choice = torch.empty(B, dtype=torch.int32, device=dev) if choice is None else choice
+    b1, b2 = _biases(b1, b2, m, dev)
+    delta_al = _out(delta_al, torch.float32, B, dev, "delta_al")
+    choice = _out(choice, torch.int32, B, dev, "choice")
+    _on(dev, pos=pos, row0=row0)
     ws = _workspace(workspace, route_workspace_bytes(B, m), dev)
     _check(whiflash_route_gather(_ptr(hidden_rows), _dtype_code(hidden_rows), total_rows, d, B,
                                  _ptr(row0), rows_per_seq, _ptr(pos), _ptr(W1), _ptr(b1), m,
@@ -383,6 +433,7 @@ def argmax_sweep(logits, *, rows=None, partials=None, stream=None):
         partials = torch.empty(need, dtype=torch.int32, device=logits.device)
     else:
         _i32(partials, "partials")
+        _on(logits.device, partials=partials)
         if partials.numel() < need:
             raise ValueError(f"partials needs {need} int32 elements")
     _check(whiflash_argmax_sweep(_ptr(logits), _dtype_code(logits), rows, V, stride,
@@ -401,6 +452,7 @@ def stream_read(logits, *, rows=None, sink=None, stream=None):
     if sink is None:
         sink = torch.zeros(1, dtype=torch.int32, device=logits.device)
     _i32(sink, "sink")
+    _on(logits.device, sink=sink)
     _check(whiflash_stream_read(_ptr(logits), _dtype_code(logits), rows, V, stride, _ptr(sink),
                                 _stream(logits, stream)))
     return sink
@@ -416,12 +468,10 @@ def verify_chain(logits, draft, *, row_argmax=True, accept_len=None, bonus=None,
     V, stride = _rows_view(logits, rows)
     _i32(draft, "draft")
     dev = logits.device
-    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
-    bonus = torch.empty(B, dtype=torch.int32, device=dev) if bonus is None else bonus
-    if row_argmax is True:
-        row_argmax = torch.empty(rows, dtype=torch.int32, device=dev)
-    elif row_argmax is False:
-        row_argmax = None
+    accept_len = _out(accept_len, torch.int32, B, dev, "accept_len")
+    bonus = _out(bonus, torch.int32, B, dev, "bonus")
+    row_argmax = _opt_out(row_argmax, rows, dev, "row_argmax")
+    _on(dev, draft=draft)
     ws = _workspace(workspace, verify_workspace_bytes(rows, V), dev)
     _check(whiflash_verify_chain(_ptr(logits), _dtype_code(logits), B, K, V, stride, _ptr(draft),
                                  _ptr(accept_len), _ptr(bonus), _ptr(row_argmax), _ptr(ws),
@@ -440,12 +490,10 @@ def verify_chain_early_exit(logits, draft, *, row_argmax=True, accept_len=None, 
     V, stride = _rows_view(logits, rows)
     _i32(draft, "draft")
     dev = logits.device
-    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
-    bonus = torch.empty(B, dtype=torch.int32, device=dev) if bonus is None else bonus
-    if row_argmax is True:
-        row_argmax = torch.empty(rows, dtype=torch.int32, device=dev)
-    elif row_argmax is False:
-        row_argmax = None
+    accept_len = _out(accept_len, torch.int32, B, dev, "accept_len")
+    bonus = _out(bonus, torch.int32, B, dev, "bonus")
+    row_argmax = _opt_out(row_argmax, rows, dev, "row_argmax")
+    _on(dev, draft=draft)
     ws = _workspace(workspace, early_exit_workspace_bytes(B, K, V), dev)
     _check(whiflash_verify_chain_early_exit(_ptr(logits), _dtype_code(logits), B, K, V, stride,
                                             _ptr(draft), _ptr(accept_len), _ptr(bonus),
@@ -467,13 +515,11 @@ def verify_tree(logits, parent, draft_ids, d2t, *, row_argmax=True, accept_len=N
     _i32(draft_ids, "draft_ids", B * N)
     _i32(d2t, "d2t")
     dev = logits.device
-    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
-    bonus = torch.empty(B, dtype=torch.int32, device=dev) if bonus is None else bonus
-    best_node = torch.empty(B, dtype=torch.int32, device=dev) if best_node is None else best_node
-    if row_argmax is True:
-        row_argmax = torch.empty(rows, dtype=torch.int32, device=dev)
-    elif row_argmax is False:
-        row_argmax = None
+    accept_len = _out(accept_len, torch.int32, B, dev, "accept_len")
+    bonus = _out(bonus, torch.int32, B, dev, "bonus")
+    best_node = _out(best_node, torch.int32, B, dev, "best_node")
+    row_argmax = _opt_out(row_argmax, rows, dev, "row_argmax")
+    _on(dev, parent=parent, draft_ids=draft_ids, d2t=d2t)
     nbytes = tree_early_exit_workspace_bytes(B, N, V) if _early else verify_workspace_bytes(rows, V)
     ws = _workspace(workspace, nbytes, dev)
     fn = whiflash_verify_tree_early_exit if _early else whiflash_verify_tree
@@ -504,13 +550,12 @@ def verify_routed(logits, row_offsets, total_rows: int, choice, chain_draft, par
     _i32(draft_ids, "draft_ids", B * N)
     _i32(d2t, "d2t")
     dev = logits.device
-    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
-    bonus = torch.empty(B, dtype=torch.int32, device=dev) if bonus is None else bonus
-    best_node = torch.empty(B, dtype=torch.int32, device=dev) if best_node is None else best_node
-    if row_argmax is True:
-        row_argmax = torch.empty(max(total_rows, 1), dtype=torch.int32, device=dev)
-    elif row_argmax is False:
-        row_argmax = None
+    accept_len = _out(accept_len, torch.int32, B, dev, "accept_len")
+    bonus = _out(bonus, torch.int32, B, dev, "bonus")
+    best_node = _out(best_node, torch.int32, B, dev, "best_node")
+    row_argmax = _opt_out(row_argmax, total_rows, dev, "row_argmax")
+    _on(dev, row_offsets=row_offsets, choice=choice, chain_draft=chain_draft, parent=parent,
+        draft_ids=draft_ids, d2t=d2t)
     nbytes = (routed_early_exit_workspace_bytes(B, K, N, total_rows, V) if _early
               else verify_workspace_bytes(total_rows, V))
     ws = _workspace(workspace, nbytes, dev)
@@ -542,8 +587,9 @@ def route_entropy(logits, pos, tau: float, *, row0=None, rows_per_seq: int = 0, 
         if row0.numel() < B:
             raise ValueError("row0 must hold at least B entries")
     dev = logits.device
-    entropy = torch.empty(B, dtype=torch.float32, device=dev) if entropy is None else entropy
-    choice = torch.empty(B, dtype=torch.int32, device=dev) if choice is None else choice
+    entropy = _out(entropy, torch.float32, B, dev, "entropy")
+    choice = _out(choice, torch.int32, B, dev, "choice")
+    _on(dev, pos=pos, row0=row0)
     ws = _workspace(workspace, entropy_workspace_bytes(B, V), dev)
     _check(whiflash_route_entropy(_ptr(logits), _dtype_code(logits), total_rows, V, stride, B,
                                   _ptr(row0), rows_per_seq, _ptr(pos), float(tau), _ptr(entropy),
@@ -563,14 +609,9 @@ def catchup_update(cur_choice, accept_len, next_choice, backlog, *, switch_flag=
     _i32(next_choice, "next_choice", B)
     _i32(backlog, "backlog", 2 * B)
     dev = backlog.device
-    if switch_flag is True:
-        switch_flag = torch.empty(B, dtype=torch.int32, device=dev)
-    elif switch_flag is False:
-        switch_flag = None
-    if catchup_len is True:
-        catchup_len = torch.empty(B, dtype=torch.int32, device=dev)
-    elif catchup_len is False:
-        catchup_len = None
+    switch_flag = _opt_out(switch_flag, B, dev, "switch_flag")
+    catchup_len = _opt_out(catchup_len, B, dev, "catchup_len")
+    _on(dev, cur_choice=cur_choice, accept_len=accept_len, next_choice=next_choice)
     _check(whiflash_catchup_update(B, _ptr(cur_choice), _ptr(accept_len), _ptr(next_choice),
                                    _ptr(backlog), _ptr(switch_flag), _ptr(catchup_len),
                                    _stream(backlog, stream)))
@@ -587,17 +628,11 @@ def round_routed(hidden, W1, b1, W2, b2, tau: float, logits, row_offsets, total_
     _device_tensor(hidden, "hidden")
     B, d = hidden.shape
     m = W1.shape[0]
-    for t, name in ((hidden, "hidden"), (W1, "W1"), (W2, "W2")):
-        _device_tensor(t, name)
-        if not t.is_contiguous() or t.dtype != hidden.dtype:
-            raise TypeError(f"{name} must be contiguous with the dtype of hidden")
+    _weights(hidden, "hidden", W1, W2)
     if tuple(W1.shape) != (m, d) or W2.numel() != m:
         raise ValueError("W1 must be [m, d] and W2 hold m elements")
     dev = hidden.device
-    if b1 is not None and (b1.dtype != torch.float32 or b1.numel() != m or not b1.is_contiguous()):
-        raise TypeError("b1 must be a contiguous float32 tensor of m elements")
-    if b2 is not None and not isinstance(b2, torch.Tensor):
-        b2 = torch.tensor([float(b2)], dtype=torch.float32, device=dev)
+    b1, b2 = _biases(b1, b2, m, dev)
     if logits.dim() != 2:
         raise ValueError("routed logits must be [total_rows, V]")
     V, stride = _rows_view(logits, total_rows)
@@ -608,16 +643,14 @@ def round_routed(hidden, W1, b1, W2, b2, tau: float, logits, row_offsets, total_
     _i32(parent, "parent", B * N)
     _i32(draft_ids, "draft_ids", B * N)
     _i32(d2t, "d2t")
-    new = lambda dt: torch.empty(B, dtype=dt, device=dev)
-    delta_al = new(torch.float32) if delta_al is None else delta_al
-    choice = new(torch.int32) if choice is None else choice
-    accept_len = new(torch.int32) if accept_len is None else accept_len
-    bonus = new(torch.int32) if bonus is None else bonus
-    best_node = new(torch.int32) if best_node is None else best_node
-    if row_argmax is True:
-        row_argmax = torch.empty(max(total_rows, 1), dtype=torch.int32, device=dev)
-    elif row_argmax is False:
-        row_argmax = None
+    delta_al = _out(delta_al, torch.float32, B, dev, "delta_al")
+    choice = _out(choice, torch.int32, B, dev, "choice")
+    accept_len = _out(accept_len, torch.int32, B, dev, "accept_len")
+    bonus = _out(bonus, torch.int32, B, dev, "bonus")
+    best_node = _out(best_node, torch.int32, B, dev, "best_node")
+    row_argmax = _opt_out(row_argmax, total_rows, dev, "row_argmax")
+    _on(dev, logits=logits, row_offsets=row_offsets, chain_draft=chain_draft, parent=parent,
+        draft_ids=draft_ids, d2t=d2t)
     nbytes = (round_early_exit_workspace_bytes(B, m, K, N, total_rows, V) if _early
               else round_workspace_bytes(B, m, total_rows, V))
     ws = _workspace(workspace, nbytes, dev)
@@ -672,16 +705,14 @@ def verify_routed_entropy(logits, row_offsets, total_rows: int, choice, chain_dr
     _i32(draft_ids, "draft_ids", B * N)
     _i32(d2t, "d2t")
     dev = logits.device
-    new = lambda dt: torch.empty(B, dtype=dt, device=dev)
-    accept_len = new(torch.int32) if accept_len is None else accept_len
-    bonus = new(torch.int32) if bonus is None else bonus
-    best_node = new(torch.int32) if best_node is None else best_node
-    entropy = new(torch.float32) if entropy is None else entropy
-    next_choice = new(torch.int32) if next_choice is None else next_choice
-    if row_argmax is True:
-        row_argmax = torch.empty(max(total_rows, 1), dtype=torch.int32, device=dev)
-    elif row_argmax is False:
-        row_argmax = None
+    accept_len = _out(accept_len, torch.int32, B, dev, "accept_len")
+    bonus = _out(bonus, torch.int32, B, dev, "bonus")
+    best_node = _out(best_node, torch.int32, B, dev, "best_node")
+    entropy = _out(entropy, torch.float32, B, dev, "entropy")
+    next_choice = _out(next_choice, torch.int32, B, dev, "next_choice")
+    row_argmax = _opt_out(row_argmax, total_rows, dev, "row_argmax")
+    _on(dev, row_offsets=row_offsets, choice=choice, chain_draft=chain_draft, parent=parent,
+        draft_ids=draft_ids, d2t=d2t)
     ws = _workspace(workspace, verify_routed_entropy_workspace_bytes(B, total_rows, V), dev)
     _check(whiflash_verify_routed_entropy(
         _ptr(logits), _dtype_code(logits), B, V, stride, _ptr(row_offsets), total_rows,
@@ -701,17 +732,11 @@ def round_chain(hidden, W1, b1, W2, b2, tau: float, logits, draft, *, row_argmax
     _device_tensor(hidden, "hidden")
     B, d = hidden.shape
     m = W1.shape[0]
-    for t, name in ((hidden, "hidden"), (W1, "W1"), (W2, "W2")):
-        _device_tensor(t, name)
-        if not t.is_contiguous() or t.dtype != hidden.dtype:
-            raise TypeError(f"{name} must be contiguous with the dtype of hidden")
+    _weights(hidden, "hidden", W1, W2)
     if tuple(W1.shape) != (m, d) or W2.numel() != m:
         raise ValueError("W1 must be [m, d] and W2 hold m elements")
     dev = hidden.device
-    if b1 is not None and (b1.dtype != torch.float32 or b1.numel() != m or not b1.is_contiguous()):
-        raise TypeError("b1 must be a contiguous float32 tensor of m elements")
-    if b2 is not None and not isinstance(b2, torch.Tensor):
-        b2 = torch.tensor([float(b2)], dtype=torch.float32, device=dev)
+    b1, b2 = _biases(b1, b2, m, dev)
     _device_tensor(draft, "draft")
     if draft.shape[0] != B:
         raise ValueError("draft must be [B, K] with the batch of hidden")
@@ -719,15 +744,12 @@ def round_chain(hidden, W1, b1, W2, b2, tau: float, logits, draft, *, row_argmax
     rows = B * (K + 1)
     V, stride = _rows_view(logits, rows)
     _i32(draft, "draft")
-    new = lambda dt: torch.empty(B, dtype=dt, device=dev)
-    delta_al = new(torch.float32) if delta_al is None else delta_al
-    choice = new(torch.int32) if choice is None else choice
-    accept_len = new(torch.int32) if accept_len is None else accept_len
-    bonus = new(torch.int32) if bonus is None else bonus
-    if row_argmax is True:
-        row_argmax = torch.empty(rows, dtype=torch.int32, device=dev)
-    elif row_argmax is False:
-        row_argmax = None
+    delta_al = _out(delta_al, torch.float32, B, dev, "delta_al")
+    choice = _out(choice, torch.int32, B, dev, "choice")
+    accept_len = _out(accept_len, torch.int32, B, dev, "accept_len")
+    bonus = _out(bonus, torch.int32, B, dev, "bonus")
+    row_argmax = _opt_out(row_argmax, rows, dev, "row_argmax")
+    _on(dev, logits=logits, draft=draft)
     nbytes = (round_chain_early_exit_workspace_bytes(B, m, K, V) if _early
               else round_chain_workspace_bytes(B, m, K, V))
     ws = _workspace(workspace, nbytes, dev)
