@@ -49,11 +49,13 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", choices=["sweep", "routed", "llama", "single"], default="sweep",
+    p.add_argument("--workload", choices=["sweep", "routed", "llama", "single", "chain32", "trees"],
+                   default="sweep",
                    help="sweep: 256 chains at Qwen3-4B shapes (default); routed: the 64/64 "
                         "chain/tree mix; llama: 256 chains at Llama-3.1-8B shapes; single: one "
                         "sequence, K = 16, float32 logits and router (latency-bound; timed by "
-                        "replaying a captured HIP graph of the steps)")
+                        "replaying a captured HIP graph of the steps); chain32: 32 chains of "
+                        "K = 16 with the router; trees: 8 EAGLE-3 trees of 61 nodes, no router")
     p.add_argument("--pool", type=int, default=None,
                    help="distinct rounds resident in HBM (default: 100 for the sweep workload, "
                         "4 for the routed early-exit mode)")
@@ -497,6 +499,94 @@ class LlamaSweep(Sweep):
         return 6, 256, 10, 128_256, 4_096, 512
 
 
+class Chain32(Sweep):
+    """32 DFlash chains of K = 16 over the 151,936-token vocabulary with the 2560 -> 1024
+    router: the batched chain configuration, 170.7 MB of bf16 logits per round."""
+    name = "batched_chain_bf16"
+
+    @staticmethod
+    def shape():
+        from synth.workloads import CONFIGS, D_QWEN3, ROUTER_M, V_QWEN3
+        c = CONFIGS["batched_chain_bf16"]
+        return c["seed"], c["B"], c["K"], V_QWEN3, D_QWEN3, ROUTER_M
+
+
+class Trees:
+    """EAGLE-3 tree verification alone: 8 trees of 61 nodes (root + 60 drafts, depth <= 8,
+    <= 10 children per node) over the 151,936-token vocabulary with the 32,000-entry d2t
+    remap, bf16 logits (148.3 MB per round).  This configuration has no router."""
+    name = "tree_bf16"
+
+    def __init__(self, torch, dev, pool):
+        from synth import make_tree_batch
+        from synth.workloads import CONFIGS, PLANT_BOOST, V_QWEN3, VD_EAGLE3
+        import drafter_routing_verification_amd as wf
+        t0 = time.time()
+        c = CONFIGS["tree_bf16"]
+        self.B, self.N, self.V = c["B"], c["N"], V_QWEN3
+        self.rows = self.B * self.N
+        self.depth_bound = 8
+        self.d = self.m = None
+        self.pool = []
+        g = torch.Generator(device=dev)
+        for rnd in range(pool):
+            tb = make_tree_batch(c["seed"], self.B, self.N, self.V, VD_EAGLE3, "bf16", 0.7,
+                                 self.depth_bound, 10, rnd, logits=False)
+            g.manual_seed(c["seed"] * 1_000_003 + rnd)
+            x = torch.randn((self.rows, self.V), generator=g, device=dev, dtype=torch.float32)
+            planted = torch.from_numpy(tb.planted.reshape(-1).astype(np.int64)).to(dev)
+            x[torch.arange(self.rows, device=dev), planted] += PLANT_BOOST
+            self.pool.append(dict(logits=x.to(torch.bfloat16),
+                                  parent=_to_dev(tb.parent, torch, dev),
+                                  ids=_to_dev(tb.draft_ids, torch, dev)))
+            del x
+            if rnd == 0:
+                self.d2t = _to_dev(tb.d2t, torch, dev)
+        new = lambda: torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.al, self.bonus, self.best = new(), new(), new()
+        self.vws = torch.empty(wf.verify_workspace_bytes(self.rows, self.V), dtype=torch.uint8,
+                               device=dev)
+        self.sweep_out = torch.empty(self.rows * wf.argmax_sweep_plan(self.rows, self.V)[0] * 2,
+                                     dtype=torch.int32, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.early = False
+        self.wf = wf
+        self.setup_s = time.time() - t0
+        self.logits_bytes = self.rows * self.V * 2
+        self.step_bytes = self.logits_bytes + 2 * self.rows * 4 + 5 * self.B * 4 + tb.d2t.size * 4
+
+    def route(self, i):
+        """No router in this configuration."""
+
+    def verify(self, i):
+        p = self.pool[i % len(self.pool)]
+        self.wf.verify_tree(p["logits"], p["parent"], p["ids"], self.d2t, row_argmax=False,
+                            accept_len=self.al, bonus=self.bonus, best_node=self.best,
+                            workspace=self.vws)
+
+    sweep = Sweep.sweep
+    stream = Sweep.stream
+
+    def check(self):
+        al = self.al.cpu().numpy()
+        assert al.min() >= 1 and al.max() <= self.depth_bound + 1
+        return float(al.mean())
+
+    def cpu_baseline(self, budget_s):
+        """The oracle on round 0 of the pool (argmax of every row, tree acceptance with the
+        d2t remap), repeated until the CPU budget is spent."""
+        import oracle
+        import torch
+        p = self.pool[0]
+        raw = p["logits"].view(torch.int16).cpu().numpy().view(np.uint16)
+        parent, ids, d2t = p["parent"].cpu().numpy(), p["ids"].cpu().numpy(), self.d2t.cpu().numpy()
+
+        def accept(t, choice):
+            oracle.verify_tree(t.reshape(self.B, self.N), parent, ids, d2t, self.V)
+        what = f"argmax of all {self.rows} rows, acceptance of {self.B} trees"
+        return _cpu_baseline(raw, "bf16", lambda: None, accept, what, budget_s)
+
+
 class Single:
     """One sequence: a DFlash block of 16 drafts over 151,936 float32 logits and the router
     2560 -> 1024 on one float32 hidden state.  A launch-latency-bound step, so its launches
@@ -694,9 +784,19 @@ def _bench_graph(args, torch, work):
 # ----------------------------------------------------------------------------- main
 
 
+# Workgroups resident at once on the GPU: 256 CUs x 8 workgroups of 4 waves (32 waves per CU).
+RESIDENT_WORKGROUPS = 2048
+
+
 def _sweep_size_fit(work, timed_loop, n):
-    """Least-squares line through the sweep kernel's durations at four launch sizes."""
+    """Least-squares line through the sweep kernel's durations at four launch sizes.  A
+    launch under two rounds of the resident workgroups is latency-bound (its duration barely
+    grows with its bytes), so when the smallest size is one the fit is skipped."""
     sizes = [work.rows * q // 4 for q in (1, 2, 3, 4)]
+    smallest = sizes[0] * work.wf.argmax_sweep_plan(sizes[0], work.V)[0]
+    if smallest < 2 * RESIDENT_WORKGROUPS:
+        return {"skipped": f"a quarter round is {smallest} workgroups, under two rounds of the "
+                           f"{RESIDENT_WORKGROUPS} resident slots: too small for a linear fit"}
     us = [timed_loop(lambda i, r=r: work.sweep(i, rows=r), n) * 1e6 for r in sizes]
     nbytes = [r * work.V * 2 for r in sizes]
     slope, fixed = np.polyfit(np.array(nbytes, np.float64), np.array(us, np.float64), 1)
@@ -734,6 +834,13 @@ def main():
             out["cpu_baseline"] = work.cpu_baseline(args.cpu_seconds)
         print(json.dumps(out), flush=True)
         return
+    elif args.workload == "chain32":
+        work = Chain32(torch, dev, args.pool or 100)
+    elif args.workload == "trees":
+        if args.mode not in ("fused", "separate"):
+            print("--workload trees times whiflash_verify_tree only", file=sys.stderr)
+            sys.exit(2)
+        work = Trees(torch, dev, args.pool or 100)
     else:
         work = Sweep(torch, dev, args.pool or 100)
     stream = torch.cuda.current_stream()
@@ -814,7 +921,7 @@ def main():
         route_s = timed_loop(work.entropy_only, K)
     else:
         verify_s = timed_loop(work.verify, K)
-        route_s = timed_loop(work.route, K)
+        route_s = timed_loop(work.route, K) if work.m else None
     # The dominant kernel alone: whiflash_argmax_sweep launches only the argmax sweep, on the
     # same stream, over the same resident rounds.
     sweep_s = None if early else timed_loop(work.sweep, K)
@@ -844,6 +951,7 @@ def main():
             "whiflash_round_routed" if fused and isinstance(work, Routed) else
             "whiflash_round_chain" if fused else
             "whiflash_route + whiflash_verify_chain_early_exit" if early else
+            "whiflash_verify_tree" if isinstance(work, Trees) else
             "whiflash_route + whiflash_verify_*")
     out = {
         "metric": "verify+route rounds/s and logits HBM GB/s (fraction of MI355X peak), 1 GPU",
@@ -864,7 +972,7 @@ def main():
                    "logits_bytes_per_round": work.logits_bytes,
                    "bytes_per_round": work.step_bytes},
         "logits_GBps": round(achieved, 1),
-        "route_us": round(route_s * 1e6, 2),
+        "route_us": None if route_s is None else round(route_s * 1e6, 2),
         "verify_us": round(verify_s * 1e6, 2),
         **({} if early else {"sweep_us": round(sweep_s * 1e6, 2)}),
         **({} if early else {"stream_read": {

@@ -1,6 +1,7 @@
 """Host-side checks of bench.py (no GPU needed): it refuses more than one GPU before
 touching a device, and its sweep size fit recovers a known fixed cost and streaming
-rate from durations that follow duration = fixed + bytes / rate exactly."""
+rate from durations that follow duration = fixed + bytes / rate exactly, and skips the fit
+when a quarter round would not fill the GPU twice over."""
 
 import os
 import subprocess
@@ -10,6 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
+import drafter_routing_verification_amd as wf  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused():
@@ -21,6 +23,7 @@ def test_more_than_one_gpu_is_refused():
 
 class _Work:
     rows, V = 4352, 151936
+    wf = wf
 
 
 def test_sweep_size_fit_recovers_a_line():
@@ -39,3 +42,13 @@ def test_sweep_size_fit_recovers_a_line():
     assert abs(fit["fixed_us"] - fixed_us) < 0.01
     assert abs(fit["steady_GBps"] - rate_gbps) < 0.5
     assert abs(fit["steady_frac"] - rate_gbps / bench.HBM_PEAK_GBS) < 1e-4
+
+
+def test_sweep_size_fit_skipped_for_latency_bound_sizes():
+    work = _Work()
+    work.rows = 544                        # 32 chains: a quarter round is 136 rows
+    work.sweep = lambda i, rows=None: None
+    blocks = 136 * wf.argmax_sweep_plan(136, work.V)[0]
+    assert blocks < 2 * bench.RESIDENT_WORKGROUPS
+    fit = bench._sweep_size_fit(work, lambda fn, n: 1e-5, 10)
+    assert f"{blocks} workgroups" in fit["skipped"] and "rows" not in fit
