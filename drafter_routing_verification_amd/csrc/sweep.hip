@@ -25,11 +25,21 @@ __device__ inline int xcd_contiguous_block() {
   return static_cast<int>(x * q + (x < r ? x : r) + k);
 }
 
-// Launches of at most kSmallLaunch workgroups fit in about two rounds of the
-// resident slots.  There few workgroups stream at once, so each thread issues
-// its whole batch of loads before comparing (sweep_chunk's kBatchTail form);
-// larger launches keep every slot busy with one load at a time per thread.
-constexpr int64_t kSmallLaunch = 4096;
+// Launches of at most kSmallLaunch workgroups fit in about four rounds of the
+// 2,048 resident slots (256 CUs x 8 workgroups of 4 waves).  There each thread
+// issues its whole batch of loads before comparing (sweep_chunk's kBatchTail
+// form); larger launches keep every slot busy with one load at a time per
+// thread.  Same-box A/B, sweep kernel alone, two interleaved trials: with the
+// switch at 8,192 instead of 4,096, 32 chains (544 rows, 5,984 workgroups)
+// 29.3-29.4 -> 27.2 us and 8 trees (488 rows, 5,368 workgroups) 26.3-26.5 ->
+// 24.4 us; 16,384 gave the same.  Batching the Llama-shape launch (25,344
+// workgroups) changed nothing (104.7-104.9 against 104.9 us), and the
+// 47,872- and 54,912-workgroup launches slowed by 4 us (190.7 -> 194.7-195.2,
+// 210.7-211.0 -> 215.5-216.0).
+#ifndef WF_SWEEP_SMALL_LAUNCH
+#define WF_SWEEP_SMALL_LAUNCH 8192
+#endif
+constexpr int64_t kSmallLaunch = WF_SWEEP_SMALL_LAUNCH;
 
 template <int DT, bool kBatch>
 __global__ __launch_bounds__(kSweepThreads) void argmax_sweep_kernel(
