@@ -8,9 +8,9 @@
 // contiguous memory.  A thread keeps its running maximum, the 16-byte vector
 // where it first reached it (strict ">" in increasing index order keeps the
 // earliest) and that vector's data, and recovers the element index from it at
-// the end.  The chunk's (max, index) pair is reduced across the wave with
-// cross-lane shuffles and across the waves in LDS; ties go to the lower
-// index at every level.
+// the end.  The chunk's (max, index) pair is reduced across the wave with DPP
+// lane moves and across the waves in LDS; ties go to the lower index at every
+// level.
 #pragma once
 
 #include <math.h>
@@ -28,6 +28,33 @@ __device__ inline void take_better(float& bv, int& bi, float v, int i) {
     bv = v;
     bi = i;
   }
+}
+
+// One step of the wave reduction: combine each lane's (bv, bi) with the pair a
+// DPP move brings from another lane (CTRL: the lane pattern; lanes of rows
+// outside ROW_MASK keep their own pair).  The compare is written as selects.
+template <int CTRL, int ROW_MASK>
+__device__ inline void dpp_take_better(float& bv, int& bi) {
+  const int ov =
+      __builtin_amdgcn_update_dpp(__float_as_int(bv), __float_as_int(bv), CTRL, ROW_MASK, 0xf, false);
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, ROW_MASK, 0xf, false);
+  const float v = __int_as_float(ov);
+  const bool t = (v > bv) | ((v == bv) & (oi < bi));  // bitwise: no short-circuit branches
+  bv = t ? v : bv;
+  bi = t ? oi : bi;
+}
+
+// (max, lowest index) over the 64 lanes of a wave, left in lane 63: pairs
+// within quads, then half rows and rows (mirrors), then lane 15 of each row
+// into the next row and lane 31 into rows 2 and 3.  The pairs are totally
+// ordered (no NaN reaches them), so the order of combination does not matter.
+__device__ inline void wave_argmax_to_lane63(float& bv, int& bi) {
+  dpp_take_better<0xB1, 0xf>(bv, bi);   // quad_perm [1,0,3,2]
+  dpp_take_better<0x4E, 0xf>(bv, bi);   // quad_perm [2,3,0,1]
+  dpp_take_better<0x141, 0xf>(bv, bi);  // row_half_mirror
+  dpp_take_better<0x140, 0xf>(bv, bi);  // row_mirror
+  dpp_take_better<0x142, 0xa>(bv, bi);  // row_bcast:15
+  dpp_take_better<0x143, 0xc>(bv, bi);  // row_bcast:31
 }
 
 // Returns the chunk's (max, index) in thread 0 (other threads: unspecified).
@@ -121,16 +148,16 @@ __device__ inline Partial sweep_chunk(int blk, const unsigned char* __restrict__
     }
   }
 
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(best, off);
-    const int oi = __shfl_xor(idx, off);
-    take_better(best, idx, ov, oi);
-  }
   __shared__ float sv[kW];
   __shared__ int si[kW];
   const int lane = tid & 63, wave = tid >> 6;
-  if (lane == 0) {
+  // DPP lane moves instead of cross-lane shuffles: each shuffle step was two
+  // ds_bpermute round trips and a branchy compare.  Same box, sweep kernel
+  // alone, two interleaved trials: 32 chains 27.1-27.2 -> 26.4-26.6 us, 8 trees
+  // 24.3-24.5 -> 24.1 us, 256 chains 186.0-186.3 -> 184.9-186.0 us,
+  // Llama-shape chains 110.1-110.3 -> 103.5 us.
+  wave_argmax_to_lane63(best, idx);
+  if (lane == 63) {
     sv[wave] = best;
     si[wave] = idx;
   }
