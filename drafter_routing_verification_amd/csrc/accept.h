@@ -11,6 +11,7 @@
 #pragma once
 
 #include "common.h"
+#include "dpp.h"
 
 namespace wf {
 
@@ -81,7 +82,14 @@ __device__ inline void merge_finish(const MergeIn& in, const Partial* __restrict
         for (int u = 0; u < kMergePer; ++u) better_partial(bv, bi, q[u].val, q[u].idx);
       }
     }
-    for (int off = G >> 1; off > 0; off >>= 1) {
+    // G is uniform, so these branches are too.  Groups of up to 16 lanes use
+    // DPP moves (quads, then half rows, then rows); wider groups finish with
+    // shuffles.  Every lane of a group ends with the group's winner.
+    if (G >= 2) dpp_better<kDppQuadXor1>(bv, bi);
+    if (G >= 4) dpp_better<kDppQuadXor2>(bv, bi);
+    if (G >= 8) dpp_better<kDppHalfMirror>(bv, bi);
+    if (G >= 16) dpp_better<kDppMirror>(bv, bi);
+    for (int off = 16; off < G; off <<= 1) {
       const float ov = __shfl_xor(bv, off);
       const int oi = __shfl_xor(bi, off);
       better_partial(bv, bi, ov, oi);

@@ -8,6 +8,7 @@
 #include "common.h"
 #include "elem.h"
 #include "router_math.h"
+#include "dpp.h"
 
 namespace wf {
 
@@ -90,10 +91,8 @@ __device__ inline void gemv_tile(int bx, int by, const void* __restrict__ hidden
   }
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
-    float s = acc[q];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == q && q < nb) zp[static_cast<int64_t>(b0 + q) * m + j] = s;
+    const float s = wave_sum_to_lane63(acc[q]);
+    if (lane == 63 && q < nb) zp[static_cast<int64_t>(b0 + q) * m + j] = s;
   }
 }
 

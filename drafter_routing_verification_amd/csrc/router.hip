@@ -4,7 +4,7 @@
 // slices s of the hidden size:
 //   - router_gemv_kernel (small batches or float32, KS = 1): one wave64 per
 //     hidden unit j streams row j of W1 once with coalesced 16-byte loads and
-//     dots it with up to 8 hidden states, reduced across the wave by shuffles.
+//     dots it with up to 8 hidden states, reduced across the wave by DPP moves.
 //   - router_mfma_kernel (bf16 batches of 16 or more): a workgroup owns a
 //     32 (j) x 64 (b) tile and one slice of the hidden size.  All of its loads
 //     are issued up front as row-contiguous 16-byte loads, staged chunk by

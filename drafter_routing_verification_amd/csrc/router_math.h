@@ -7,6 +7,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "dpp.h"
 
 namespace wf {
 
@@ -95,10 +96,9 @@ __device__ inline float router_finish_compute(const FinishIn& first, const float
     finish_load_pass<DT>(in, zp, KS, B, m, b, base, b1, W2, b2, sel);
     acc = finish_fold_pass(in, KS, m, base, acc);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  acc = wave_sum_to_lane63(acc);
   __syncthreads();  // red may still be in use by the caller
-  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  if ((tid & 63) == 63) red[tid >> 6] = acc;
   __syncthreads();
   float v = red[0];
   for (int w = 1; w < kWaves; ++w) v += red[w];

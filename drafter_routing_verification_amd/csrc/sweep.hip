@@ -2,6 +2,7 @@
 // (the per-chunk work is in sweep_body.h).
 #include "common.h"
 #include "sweep_body.h"
+#include "dpp.h"
 
 #ifndef WF_SWEEP_THREADS
 #define WF_SWEEP_THREADS 256
@@ -87,10 +88,9 @@ __global__ __launch_bounds__(kSweepThreads) void stream_read_kernel(
       acc ^= d[0] ^ d[1] ^ d[2] ^ d[3];
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
   __shared__ unsigned sx[kSweepThreads / 64];
-  if ((threadIdx.x & 63) == 0) sx[threadIdx.x >> 6] = acc;
+  acc = wave_xor_to_lane63(acc);  // the same DPP reduction shape as the sweep's
+  if ((threadIdx.x & 63) == 63) sx[threadIdx.x >> 6] = acc;
   __syncthreads();
   if (blk == 0 && threadIdx.x == 0) {
     unsigned t = 0;

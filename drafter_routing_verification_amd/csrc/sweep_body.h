@@ -17,6 +17,7 @@
 
 #include "common.h"
 #include "elem.h"
+#include "dpp.h"
 
 namespace wf {
 
@@ -30,32 +31,9 @@ __device__ inline void take_better(float& bv, int& bi, float v, int i) {
   }
 }
 
-// One step of the wave reduction: combine each lane's (bv, bi) with the pair a
-// DPP move brings from another lane (CTRL: the lane pattern; lanes of rows
-// outside ROW_MASK keep their own pair).  The compare is written as selects.
-template <int CTRL, int ROW_MASK>
-__device__ inline void dpp_take_better(float& bv, int& bi) {
-  const int ov =
-      __builtin_amdgcn_update_dpp(__float_as_int(bv), __float_as_int(bv), CTRL, ROW_MASK, 0xf, false);
-  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, ROW_MASK, 0xf, false);
-  const float v = __int_as_float(ov);
-  const bool t = (v > bv) | ((v == bv) & (oi < bi));  // bitwise: no short-circuit branches
-  bv = t ? v : bv;
-  bi = t ? oi : bi;
-}
-
-// (max, lowest index) over the 64 lanes of a wave, left in lane 63: pairs
-// within quads, then half rows and rows (mirrors), then lane 15 of each row
-// into the next row and lane 31 into rows 2 and 3.  The pairs are totally
-// ordered (no NaN reaches them), so the order of combination does not matter.
-__device__ inline void wave_argmax_to_lane63(float& bv, int& bi) {
-  dpp_take_better<0xB1, 0xf>(bv, bi);   // quad_perm [1,0,3,2]
-  dpp_take_better<0x4E, 0xf>(bv, bi);   // quad_perm [2,3,0,1]
-  dpp_take_better<0x141, 0xf>(bv, bi);  // row_half_mirror
-  dpp_take_better<0x140, 0xf>(bv, bi);  // row_mirror
-  dpp_take_better<0x142, 0xa>(bv, bi);  // row_bcast:15
-  dpp_take_better<0x143, 0xc>(bv, bi);  // row_bcast:31
-}
+// The wave step of the chunk's reduction is wave_argmax_to_lane63 (dpp.h).  A
+// thread's running maximum never holds NaN (a NaN vector maximum never beats
+// it), so the pairs it combines are totally ordered.
 
 // Returns the chunk's (max, index) in thread 0 (other threads: unspecified).
 // NT threads per workgroup (a multiple of 64).  Two forms of the stream:
