@@ -59,6 +59,18 @@ def test_chain_large_vocab(dtype, V):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chain_one_row_per_sequence_widest_merge(dtype):
+    """K = 0 over 1,000,003 tokens: one row per sequence, so the verify call's sweep cuts
+    each row into 256 chunks and the acceptance merges them with 64-lane groups (DPP moves
+    within rows of 16 lanes, then shuffles at offsets 16 and 32)."""
+    V = 1000003
+    print(f"one-row chains, widest merge, dtype={dtype}", flush=True)
+    cb = make_chain_batch(17, 3, 0, V, dtype)
+    t, al = _chain_both(cb.logits, dtype, cb.draft, V)
+    assert np.all(al == 1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_planted_far_ties_and_tail(dtype):
     V = 1000003
     print(f"large-vocab planted rows dtype={dtype}", flush=True)
