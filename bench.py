@@ -41,7 +41,7 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "argmax_sweep_traffic.json")
 # Sources of the argmax sweep kernel: a change to any of them voids the stored counters.
 SWEEP_SRCS = [os.path.join(ROOT, "drafter_routing_verification_amd", "csrc", f)
-              for f in ("sweep.hip", "sweep_body.h", "elem.h")]
+              for f in ("sweep.hip", "sweep_body.h", "elem.h", "dpp.h")]
 
 
 def _parse():

@@ -222,9 +222,8 @@ __device__ inline void tree_accept(const TreeIn& in, const int* t_s, int N, int*
     const int u = tid + k * kThreads;
     if (u < N && ok[u]) key = max(key, (dep[u] << 16) | (0xffff - u));
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) key = max(key, __shfl_xor(key, off));
-  if ((tid & 63) == 0) red[tid >> 6] = key;
+  key = wave_max_to_lane63(key);
+  if ((tid & 63) == 63) red[tid >> 6] = key;
   __syncthreads();
   if (tid == 0) {
     int k = red[0];

@@ -7,7 +7,9 @@
 //     8-lane half row / 16-lane row;
 //   row_bcast:15 (rows 1 and 3) / row_bcast:31 (rows 2 and 3): lane 15 of the
 //     row before / lane 31, into the lanes of the rows named.
-// Lanes of rows outside a step's row mask keep their own value.
+// Lanes of rows outside a step's row mask keep their own value, so in the two
+// broadcast steps they combine with themselves: harmless for max, and for sums
+// and merges only in lanes that do not feed lane 63, which holds the result.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,6 +41,17 @@ __device__ inline float wave_sum_to_lane63(float x) {
   x += dpp_mov<kDppMirror>(x);
   x += dpp_mov<kDppBcast15, 0xa>(x);
   x += dpp_mov<kDppBcast31, 0xc>(x);
+  return x;
+}
+
+// Maximum over the 64 lanes of a wave, left in lane 63.
+__device__ inline int wave_max_to_lane63(int x) {
+  x = max(x, dpp_mov<kDppQuadXor1>(x));
+  x = max(x, dpp_mov<kDppQuadXor2>(x));
+  x = max(x, dpp_mov<kDppHalfMirror>(x));
+  x = max(x, dpp_mov<kDppMirror>(x));
+  x = max(x, dpp_mov<kDppBcast15, 0xa>(x));
+  x = max(x, dpp_mov<kDppBcast31, 0xc>(x));
   return x;
 }
 

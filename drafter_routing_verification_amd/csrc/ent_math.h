@@ -10,6 +10,8 @@
 
 #include <math.h>
 
+#include "dpp.h"
+
 namespace wf {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -34,8 +36,21 @@ __device__ inline void ent_merge(Ent& a, const Ent& b) {
   a.m = M;
 }
 
-__device__ inline Ent ent_shfl_xor(const Ent& e, int off) {
-  return Ent{__shfl_xor(e.m, off), __shfl_xor(e.S, off), __shfl_xor(e.U, off)};
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline void ent_dpp_merge(Ent& a) {
+  const Ent o{dpp_mov<CTRL, ROW_MASK>(a.m), dpp_mov<CTRL, ROW_MASK>(a.S),
+              dpp_mov<CTRL, ROW_MASK>(a.U)};
+  ent_merge(a, o);
+}
+
+// Merge of the 64 lanes' streams of a wave, left in lane 63 (a fixed order).
+__device__ inline void wave_ent_to_lane63(Ent& a) {
+  ent_dpp_merge<kDppQuadXor1>(a);
+  ent_dpp_merge<kDppQuadXor2>(a);
+  ent_dpp_merge<kDppHalfMirror>(a);
+  ent_dpp_merge<kDppMirror>(a);
+  ent_dpp_merge<kDppBcast15, 0xa>(a);
+  ent_dpp_merge<kDppBcast31, 0xc>(a);
 }
 
 // Raises the running maximum of a to mv (mv > a.m), rescaling S and U.

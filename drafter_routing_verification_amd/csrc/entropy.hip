@@ -63,13 +63,9 @@ __global__ __launch_bounds__(kThreads) void entropy_partial_kernel(
       }
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const Ent o = ent_shfl_xor(acc, off);
-    ent_merge(acc, o);
-  }
+  wave_ent_to_lane63(acc);
   __shared__ Ent red[kWaves];
-  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  if ((tid & 63) == 63) red[tid >> 6] = acc;
   __syncthreads();
   if (tid == 0) {
     Ent t = red[0];
@@ -91,12 +87,8 @@ __global__ __launch_bounds__(kThreads) void entropy_finish_kernel(
     const float4 p = part[static_cast<int64_t>(b) * splits + s];
     ent_merge(acc, Ent{p.x, p.y, p.z});
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const Ent o = ent_shfl_xor(acc, off);
-    ent_merge(acc, o);
-  }
-  if (lane == 0) {
+  wave_ent_to_lane63(acc);
+  if (lane == 63) {
     const bool valid = select_row(row0, rows_per_seq, pos, total_rows, b) >= 0 && acc.S > 0.f;
     const float H = valid ? ent_value(acc) : NAN;
     entropy[b] = H;
