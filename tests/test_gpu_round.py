@@ -131,6 +131,27 @@ def test_round_chain_few_sequences(hd, ld, B):
     _chain_round(r, cb, padded_logits(cb.logits, (V + 7) // 8 * 8 + 8), b1, -0.125)
 
 
+def test_round_chain_batched_chain_config():
+    """The 32-chain configuration at full size: K = 16 over 151,936 bf16 logits and the
+    2560 -> 1024 bf16 router."""
+    print("round_chain batched_chain_bf16", flush=True)
+    batch, r = make_config("batched_chain_bf16")
+    _chain_round(r, batch, dev(batch.logits), r.b1, 0.0)
+
+
+@pytest.mark.parametrize("B", [12, 16, 24, 32, 33])
+def test_round_chain_mid_batches(B):
+    """12 to 33 sequences on 16-byte aligned operands, around the MFMA router's 16-sequence
+    switch (the GEMV router below it, two launches per round from 9 sequences on)."""
+    from synth import make_chain_batch
+    print(f"round_chain batch tiles B={B}", flush=True)
+    r = make_router_inputs(B + 500, B, 2560, 1024, "bf16")
+    b1 = (np.random.default_rng(B + 2).standard_normal(r.m) * 0.5).astype(np.float32)
+    V = 20011
+    cb = make_chain_batch(B + 501, B, 16, V, "bf16")
+    _chain_round(r, cb, padded_logits(cb.logits, (V + 7) // 8 * 8 + 8), b1, 0.0)
+
+
 def test_round_chain_single_sequence_f32():
     """The single-sequence float32 workload at full size: K = 16 over 151,936 float32 logits
     and the 2560 -> 1024 router on one float32 hidden state."""
