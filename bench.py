@@ -74,6 +74,10 @@ def _parse():
                    help="skip the sweep launches over partial rounds (profiler runs use this, so "
                         "every argmax_sweep_kernel dispatch they record covers whole rounds)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--router-width", type=int, default=None,
+                   help="router hidden width m for the chain workloads (sweep, chain32, llama); "
+                        "default 1024 (512 for llama).  The paper's router uses m = d/8: 320 "
+                        "at the Qwen3-4B hidden size 2560")
     return p.parse_args()
 
 
@@ -121,6 +125,15 @@ def _argmax_worker(conn, raw, dtype):
 
 
 def _cpu_model() -> str:
+    """The host CPU's model name as lscpu reports it (else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        res = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for line in res.stdout.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -131,29 +144,42 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+# The GPU hosts give one job with one GPU a share of 16 CPUs, however many the host has or
+# os.sched_getaffinity shows, so the parallel oracle leg runs at most this many processes.
+CPU_SHARE = 16
+
+
 def _cpu_baseline(raw, dtype, route, accept, what, budget_s):
-    """Whole rounds of the oracle (route() -> choices; the row argmax of every logits row;
-    accept(t, choices)), timed on the host cores in two ways: one process on one thread, and
-    P processes (P - 1 children each take a contiguous block of rows for the argmax while the
-    parent runs the router, then the parent runs the acceptance).  Process start-up and the
-    hand-over of the rows to the children are outside the timed rounds."""
+    """Whole rounds of the oracle (route() -> (delta_al, choices); the row argmax of every
+    logits row; accept(t, choices) -> dict of results), timed on the host cores in two ways:
+    one process on one thread, and P processes (P - 1 children each take a contiguous block of
+    rows for the argmax while the parent runs the router, then the parent runs the
+    acceptance).  Process start-up and the hand-over of the rows to the children are outside
+    the timed rounds.  Returns (baseline, results of the first round), the latter for the
+    bench's parity check of the same round on the GPU."""
     import multiprocessing as mp
     import oracle
     from threadpoolctl import threadpool_limits
-    rounds, spent = 0, 0.0
+    rounds, spent, first = 0, 0.0, None
     with threadpool_limits(limits=1):
         while spent < budget_s:
             t0 = time.perf_counter()
-            choice = route()
-            accept(oracle.row_argmax(raw, dtype), choice)
+            dal, choice = route()
+            t = oracle.row_argmax(raw, dtype)
+            res = accept(t, choice)
             spent += time.perf_counter() - t0
             rounds += 1
+            if first is None:
+                first = dict(res, rows=t, dal=dal, choice=choice)
+    affinity = len(os.sched_getaffinity(0))
+    P = min(CPU_SHARE, affinity)
     out = {"value": rounds / spent, "unit": "rounds/s", "cores": 1, "kind": "oracle",
            "sample": f"{rounds} whole rounds ({what}); {spent:.1f} s of CPU work on one thread",
-           "cpu_model": _cpu_model()}
-    P = min(16, len(os.sched_getaffinity(0)))
+           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(), "affinity_cpus": affinity,
+           "parallel_cap": f"{CPU_SHARE} processes: the CPU share a one-GPU job gets on the "
+                           "GPU host"}
     if P < 2:
-        return out
+        return out, first
     ctx = mp.get_context("spawn")
     conns, procs = [], []
     try:
@@ -174,7 +200,7 @@ def _cpu_baseline(raw, dtype, route, accept, what, budget_s):
                 t0 = time.perf_counter()
                 for c in conns:
                     c.send(True)
-                choice = route()
+                _, choice = route()
                 accept(np.concatenate([c.recv() for c in conns]), choice)
                 pspent += time.perf_counter() - t0
                 prounds += 1
@@ -190,7 +216,44 @@ def _cpu_baseline(raw, dtype, route, accept, what, budget_s):
                        "processes": P, "kind": "oracle",
                        "sample": f"{prounds} whole rounds; {P - 1} processes split the rows for "
                                  f"the argmax while the parent runs the router; {pspent:.1f} s"}
-    return out
+    return out, first
+
+
+def _parity(gpu: dict, ref: dict, tau, rtol: float) -> dict:
+    """Round 0 of the timed workload on the GPU against the oracle's first baseline round.
+    Bit-exact: accept lengths, bonus tokens, best nodes and every row argmax (rows an
+    early-exit schedule skipped hold -1 and are not compared); routing choices too, except
+    for sequences whose exact gain lies within 1e-3 of the threshold (those, and what they
+    route to, are not compared); delta-AL within rtol * max(|ref|, 1)."""
+    bad = []
+    detail = {"round": 0}
+    far = None
+    if ref.get("dal") is not None and gpu.get("dal") is not None:
+        e = np.asarray(ref["dal"], np.float64)
+        err = np.abs(np.asarray(gpu["dal"], np.float64) - e) / np.maximum(np.abs(e), 1.0)
+        detail["dal_max_rel_err"] = float(err.max())
+        detail["dal_tolerance"] = rtol
+        if not err.max() <= rtol:
+            bad.append(f"delta-AL error {err.max():.3e} > {rtol}")
+        far = np.abs(e - float(np.float32(tau))) >= 1e-3
+        detail["sequences_within_1e-3_of_threshold"] = int((~far).sum())
+        if not np.array_equal(np.asarray(gpu["choice"])[far], np.asarray(ref["choice"])[far]):
+            bad.append("routing choices differ")
+    # Routed rounds verify with the GPU's own choices; sequences in the band may go either way.
+    seq = far if (far is not None and gpu.get("routed")) else slice(None)
+    for key in ("al", "bonus", "best"):
+        if key in ref:
+            g, r = np.asarray(gpu[key]), np.asarray(ref[key])
+            if not np.array_equal(g[seq], r[seq]):
+                bad.append(f"{key} differs at {int((g[seq] != r[seq]).sum())} sequences")
+    g_rows, r_rows = np.asarray(gpu["rows"]), np.asarray(ref["rows"])
+    read = g_rows != -1
+    detail["rows_compared"] = int(read.sum())
+    if not np.array_equal(g_rows[read], r_rows[read]):
+        bad.append(f"row argmax differs at {int((g_rows[read] != r_rows[read]).sum())} rows")
+    detail["sequences"] = int(np.asarray(ref["al"]).shape[0])
+    detail["status"] = "ok" if not bad else "FAILED: " + "; ".join(bad)
+    return detail
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -350,14 +413,35 @@ class Routed:
         b, r = self.batch, self.router
 
         def route():
-            return oracle.route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)[1]
+            return oracle.route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)
 
         def accept(t, choice):
-            oracle.verify_routed(t, b.offsets, choice, b.K, b.chain_draft, b.N, b.parent,
-                                 b.draft_ids, b.d2t, b.V)
+            al, bo, be = oracle.verify_routed(t, b.offsets, choice, b.K, b.chain_draft, b.N,
+                                              b.parent, b.draft_ids, b.d2t, b.V)
+            return {"al": al, "bonus": bo, "best": be}
         what = (f"router on {b.B} hidden states, argmax of all {self.rows} rows, routed "
                 "acceptance")
         return _cpu_baseline(b.logits, b.dtype, route, accept, what, budget_s)
+
+    def gpu_round0(self, fused, entropy):
+        """Round 0 through the timed step's own entry point, with every row's argmax."""
+        r, p, wf = self.router, self.pool[0], self.wf
+        H = lambda t: t.cpu().numpy()
+        common = (p["logits"], self.offsets, self.rows)
+        tree = (p["chain_draft"], p["parent"], p["draft_ids"], self.d2t)
+        if entropy:
+            al, bo, be, rows = wf.verify_routed(*common, self.layout, *tree)[:4]
+            return {"al": H(al), "bonus": H(bo), "best": H(be), "rows": H(rows)}
+        if fused:
+            fn = wf.round_routed_early_exit if self.early else wf.round_routed
+            dal, ch, al, bo, be, rows = fn(self.hidden, self.W1, self.b1, self.W2, self.b2, r.tau,
+                                           *common, *tree)
+        else:
+            dal, ch = wf.route(self.hidden, self.W1, self.b1, self.W2, self.b2, r.tau)
+            fn = wf.verify_routed_early_exit if self.early else wf.verify_routed
+            al, bo, be, rows = fn(*common, ch, *tree)
+        return {"dal": H(dal), "choice": H(ch), "al": H(al), "bonus": H(bo), "best": H(be),
+                "rows": H(rows), "routed": True}
 
 
 class Sweep:
@@ -370,12 +454,14 @@ class Sweep:
         c = CONFIGS["sweep_bf16"]
         return c["seed"], c["B"], c["K"], V_QWEN3, D_QWEN3, ROUTER_M
 
-    def __init__(self, torch, dev, pool):
+    def __init__(self, torch, dev, pool, router_width=None):
         from synth import make_chain_batch, make_router_inputs
         from synth.workloads import PLANT_BOOST
         import drafter_routing_verification_amd as wf
         t0 = time.time()
         seed, self.B, self.K, self.V, self.d, m = self.shape()
+        if router_width:
+            m = router_width
         self.rows = self.B * (self.K + 1)
         self.pool = []
         g = torch.Generator(device=dev)
@@ -480,12 +566,27 @@ class Sweep:
         hidden, W1, W2, b1 = bits(p["hidden"]), bits(self.W1), bits(self.W2), self.b1.cpu().numpy()
 
         def route():
-            return oracle.route(hidden, W1, b1, W2, 0.0, self.tau, "bf16")[1]
+            return oracle.route(hidden, W1, b1, W2, 0.0, self.tau, "bf16")
 
         def accept(t, choice):
-            oracle.verify_chain(t.reshape(self.B, self.K + 1), draft)
+            al, bo = oracle.verify_chain(t.reshape(self.B, self.K + 1), draft)
+            return {"al": al, "bonus": bo}
         what = f"router on {self.B} hidden states, argmax of all {self.rows} rows, chain acceptance"
         return _cpu_baseline(raw, "bf16", route, accept, what, budget_s)
+
+    def gpu_round0(self, fused, entropy=False):
+        """Round 0 through the timed step's own entry point, with every row's argmax."""
+        p, wf = self.pool[0], self.wf
+        H = lambda t: t.cpu().numpy()
+        if fused:
+            fn = wf.round_chain_early_exit if self.early else wf.round_chain
+            dal, ch, al, bo, rows = fn(p["hidden"], self.W1, self.b1, self.W2, None, self.tau,
+                                       p["logits"], p["draft"])
+        else:
+            dal, ch = wf.route(p["hidden"], self.W1, self.b1, self.W2, None, self.tau)
+            fn = wf.verify_chain_early_exit if self.early else wf.verify_chain
+            al, bo, rows = fn(p["logits"], p["draft"])
+        return {"dal": H(dal), "choice": H(ch), "al": H(al), "bonus": H(bo), "rows": H(rows)}
 
 
 class LlamaSweep(Sweep):
@@ -582,9 +683,16 @@ class Trees:
         parent, ids, d2t = p["parent"].cpu().numpy(), p["ids"].cpu().numpy(), self.d2t.cpu().numpy()
 
         def accept(t, choice):
-            oracle.verify_tree(t.reshape(self.B, self.N), parent, ids, d2t, self.V)
+            al, bo, be = oracle.verify_tree(t.reshape(self.B, self.N), parent, ids, d2t, self.V)
+            return {"al": al, "bonus": bo, "best": be}
         what = f"argmax of all {self.rows} rows, acceptance of {self.B} trees"
-        return _cpu_baseline(raw, "bf16", lambda: None, accept, what, budget_s)
+        return _cpu_baseline(raw, "bf16", lambda: (None, None), accept, what, budget_s)
+
+    def gpu_round0(self, fused=False, entropy=False):
+        p = self.pool[0]
+        H = lambda t: t.cpu().numpy()
+        al, bo, be, rows = self.wf.verify_tree(p["logits"], p["parent"], p["ids"], self.d2t)
+        return {"al": H(al), "bonus": H(bo), "best": H(be), "rows": H(rows)}
 
 
 class Single:
@@ -668,12 +776,20 @@ class Single:
         batch, r = self.host0
 
         def route():
-            return oracle.route(r.hidden, r.W1, r.b1, r.W2, np.float32(r.b2), r.tau, "f32")[1]
+            return oracle.route(r.hidden, r.W1, r.b1, r.W2, np.float32(r.b2), r.tau, "f32")
 
         def accept(t, choice):
-            oracle.verify_chain(t.reshape(self.B, self.K + 1), batch.draft)
+            al, bo = oracle.verify_chain(t.reshape(self.B, self.K + 1), batch.draft)
+            return {"al": al, "bonus": bo}
         what = f"router on one float32 hidden state, argmax of all {self.rows} float32 rows, chain acceptance"
         return _cpu_baseline(batch.logits, "f32", route, accept, what, budget_s)
+
+    def gpu_round0(self, fused=True, entropy=False):
+        p = self.pool[0]
+        H = lambda t: t.cpu().numpy()
+        dal, ch, al, bo, rows = self.wf.round_chain(p["hidden"], p["W1"], p["b1"], p["W2"], None,
+                                                    self.tau, p["logits"], p["draft"])
+        return {"dal": H(dal), "choice": H(ch), "al": H(al), "bonus": H(bo), "rows": H(rows)}
 
 
 def _graph_loop(torch, work, fn, outs, n):
@@ -810,6 +926,11 @@ def _sweep_size_fit(work, timed_loop, n):
 
 def main():
     args = _parse()
+    if args.router_width is not None and (args.router_width < 1 or
+                                          args.workload not in ("sweep", "chain32", "llama")):
+        print("--router-width takes a positive width and applies to the sweep, chain32 and "
+              "llama workloads", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (sequences are "
               "independent, so N GPUs would each run this step on B/N sequences)", file=sys.stderr)
@@ -820,7 +941,7 @@ def main():
     if args.workload == "routed":
         work = Routed(torch, dev, (args.pool or 4) if args.mode == "early-exit" else 1)
     elif args.workload == "llama":
-        work = LlamaSweep(torch, dev, args.pool or 100)
+        work = LlamaSweep(torch, dev, args.pool or 100, args.router_width)
     elif args.workload == "single":
         if args.mode != "fused":
             print("--workload single times whiflash_round_chain (--mode fused) only",
@@ -830,19 +951,17 @@ def main():
         print(f"# workload {work.name}: inputs resident in HBM ({work.setup_s:.1f} s setup)",
               file=sys.stderr, flush=True)
         out = _bench_graph(args, torch, work)
-        if not args.no_cpu_baseline:
-            out["cpu_baseline"] = work.cpu_baseline(args.cpu_seconds)
-        print(json.dumps(out), flush=True)
+        _finish(out, work, args, fused=True, entropy=False, rtol=1e-4, tau=work.tau)
         return
     elif args.workload == "chain32":
-        work = Chain32(torch, dev, args.pool or 100)
+        work = Chain32(torch, dev, args.pool or 100, args.router_width)
     elif args.workload == "trees":
         if args.mode not in ("fused", "separate"):
             print("--workload trees times whiflash_verify_tree only", file=sys.stderr)
             sys.exit(2)
         work = Trees(torch, dev, args.pool or 100)
     else:
-        work = Sweep(torch, dev, args.pool or 100)
+        work = Sweep(torch, dev, args.pool or 100, args.router_width)
     stream = torch.cuda.current_stream()
     print(f"# workload {work.name}: inputs resident in HBM ({work.setup_s:.1f} s setup)",
           file=sys.stderr, flush=True)
@@ -1000,9 +1119,25 @@ def main():
             "traffic": traffic,
         },
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = work.cpu_baseline(args.cpu_seconds)
+    tau = work.router.tau if isinstance(work, Routed) else getattr(work, "tau", None)
+    _finish(out, work, args, fused=fused, entropy=entropy, rtol=2e-2, tau=tau)
+
+
+def _finish(out, work, args, fused, entropy, rtol, tau):
+    """The CPU baseline and, from its first round, the parity check of round 0; then the line.
+    A parity failure prints the line with the failure and exits with status 1."""
+    if args.no_cpu_baseline:
+        out["parity"] = "not checked (--no-cpu-baseline: the oracle runs in the CPU baseline)"
+        print(json.dumps(out), flush=True)
+        return
+    gpu0 = work.gpu_round0(fused, entropy)
+    out["cpu_baseline"], ref0 = work.cpu_baseline(args.cpu_seconds)
+    detail = _parity(gpu0, ref0, tau, rtol)
+    out["parity"] = "ok" if detail["status"] == "ok" else detail["status"]
+    out["parity_detail"] = detail
     print(json.dumps(out), flush=True)
+    if detail["status"] != "ok":
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -18,6 +18,7 @@ from .workloads import (  # noqa: F401
     make_chain_batch,
     make_tree_batch,
     make_router_inputs,
+    negate_second_layer,
     make_routed_batch,
     make_d2t,
     make_config,

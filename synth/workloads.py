@@ -243,6 +243,23 @@ def make_router_inputs(seed: int, B: int, d: int = D_QWEN3, m: int = ROUTER_M,
                         np.zeros(m, np.float32), _materialise(W2, dtype), float(np.float32(b2)))
 
 
+def negate_second_layer(r: RouterInputs) -> RouterInputs:
+    """The same router with W2, b2 and tau negated (sign flips only, exact in bf16 and f32).
+
+    Its gain is the negated gain and its threshold the negated threshold, so a
+    sequence with gain g takes choice 1 iff -g > -tau, i.e. iff g < tau.  This is
+    how the routed workload is posed under the reading that sends gains above
+    the threshold to the DFlash chain, with the library's fixed convention
+    (choice 1 = EAGLE-3 iff gain > threshold) left unchanged.
+    """
+    if r.dtype == "bf16":
+        W2 = (np.asarray(r.W2, np.uint16) ^ np.uint16(0x8000)).astype(np.uint16)
+    else:
+        W2 = -np.asarray(r.W2, np.float32)
+    return RouterInputs(r.B, r.d, r.m, r.dtype, r.hidden, r.W1, r.b1, W2,
+                        float(-np.float32(r.b2)), float(-np.float32(r.tau)))
+
+
 # --------------------------------------------------------------------------- routed
 
 
@@ -319,8 +336,16 @@ CONFIGS = {
 }
 
 
-def make_config(name: str, rnd: int = 0, logits: bool = True, V: int = V_QWEN3):
-    """Returns (batch, router_inputs_or_None) for one of the five workloads."""
+def make_config(name: str, rnd: int = 0, logits: bool = True, V: int = V_QWEN3,
+                polarity: str = "paper"):
+    """Returns (batch, router_inputs_or_None) for one of the five workloads.
+
+    polarity applies to the routed workload only.  "paper": a gain above the
+    threshold picks the EAGLE-3 tree (WhiFlash paper, section 3.3.2, decision
+    rule pi(h_t, tau_neural)).  "literal": a gain above the threshold is
+    verified as a DFlash chain; the router comes from negate_second_layer and
+    every sequence swaps its layout (same hidden states, exact 64/64 split, same
+    1e-3 margin)."""
     c = CONFIGS[name]
     seed = c["seed"]
     if c["kind"] == "chain":
@@ -330,10 +355,16 @@ def make_config(name: str, rnd: int = 0, logits: bool = True, V: int = V_QWEN3):
     if c["kind"] == "tree":
         return make_tree_batch(seed, c["B"], c["N"], V, VD_EAGLE3, c["dtype"], 0.7, 8, 10,
                                rnd, logits), None
+    if polarity not in ("paper", "literal"):
+        raise ValueError(f"unknown polarity {polarity!r}")
     cal = routed_calibration()
     router = make_router_inputs(seed, c["B"], dtype=c["dtype"], rnd=rnd, b2=cal["b2"])
-    batch = make_routed_batch(seed, np.asarray(cal["choice"], np.int32), c["K"], c["N"], V,
-                              VD_EAGLE3, c["dtype"], 0.8, 0.7, rnd, logits)
+    layout = np.asarray(cal["choice"], np.int32)
+    if polarity == "literal":
+        router = negate_second_layer(router)
+        layout = 1 - layout
+    batch = make_routed_batch(seed, layout, c["K"], c["N"], V, VD_EAGLE3, c["dtype"], 0.8, 0.7,
+                              rnd, logits)
     batch.router = router
     return batch, router
 

@@ -27,3 +27,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The largest Delta-AL error the router comparisons saw, per input element type."""
+    mod = sys.modules.get("gpu_helpers")
+    seen = getattr(mod, "OBSERVED_DAL_ERR", None) if mod else None
+    if seen:
+        for dtype, (err, batch) in sorted(seen.items()):
+            terminalreporter.write_line(
+                f"largest delta-AL error, {dtype} inputs: {err:.3e} relative "
+                f"(tolerance rule |gpu - ref| <= rtol * max(|ref|, 1); batch {batch})")

@@ -66,9 +66,10 @@ def test_tree_bf16():
     assert np.array_equal(al, e[0]) and np.array_equal(bo, e[1]) and np.array_equal(be, e[2])
 
 
-def test_routed_bf16():
-    print("workload routed_bf16", flush=True)
-    batch, router = make_config("routed_bf16")
+@pytest.mark.parametrize("polarity", ["paper", "literal"])
+def test_routed_bf16(polarity):
+    print(f"workload routed_bf16, {polarity} polarity", flush=True)
+    batch, router = make_config("routed_bf16", polarity=polarity)
     ch_gpu, ch_ref = _route(router)
     assert np.array_equal(ch_ref, batch.layout_choice)
     # the device choice of the router drives the dispatch, as in the benchmark
@@ -118,3 +119,29 @@ def test_llama_shapes_route_chain_tree():
     e = oracle.verify_tree(t.reshape(8, 61), tb.parent, tb.draft_ids, tb.d2t, LLAMA_V)
     assert np.array_equal(out[3], t)
     assert all(np.array_equal(a, b) for a, b in zip(out[:3], e))
+
+
+def test_router_paper_width_mfma_256():
+    """The paper's router shape, 2560 -> 320 (WhiFlash paper, Appendix A: m = d/8; Table 6:
+    0.82M parameters), at 256 sequences, where whiflash_route takes its MFMA path."""
+    from synth import make_router_inputs
+    print("router 2560 -> 320, 256 sequences", flush=True)
+    _route(make_router_inputs(14, 256, 2560, 320, "bf16"))
+
+
+# The router's documented arithmetic is float32 (products of bf16 inputs are exact in
+# float32; sums, GELU and the second layer run in float32), so beyond the 2e-2 contract for
+# bf16 the error should stay at float32 level.  A float32 dot product over d terms
+# accumulates rounding errors of order sqrt(d) * 2^-24 relative to its partial sums
+# (about 3e-6 at d = 2560 for these N(0, 1/d) weights); the second layer averages m such
+# errors with weights N(0, 1/m).  1e-4, the float32 contract, leaves a wide margin.
+@pytest.mark.parametrize("name", ["batched_chain_bf16", "routed_bf16", "sweep_bf16"])
+def test_router_bf16_error_at_float32_level(name):
+    print(f"router error level, {name}", flush=True)
+    _, r = make_config(name, logits=False)
+    dal, ch = (host(x) for x in wf.route(dev(r.hidden), dev(r.W1), dev(r.b1), dev(r.W2),
+                                         float(r.b2), r.tau))
+    e_dal, _ = oracle.route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)
+    err = np.abs(dal - e_dal) / np.maximum(np.abs(e_dal), 1.0)
+    print(f"  max relative error {err.max():.3e}", flush=True)
+    assert err.max() <= 1e-4

@@ -2,6 +2,8 @@
 launches) against the oracle's route followed by its routed verification, and
 agreement with the two separate GPU calls (the router may be summed in another order)."""
 
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -66,12 +68,23 @@ def test_round_small(B, d, m):
     assert np.all(out[2][mism] == 0) and np.all(out[2][~mism] >= 1)
 
 
-def test_round_routed_workload():
-    print("round on routed_bf16", flush=True)
-    batch, r = make_config("routed_bf16")
+@pytest.mark.parametrize("polarity", ["paper", "literal"])
+def test_round_routed_workload(polarity):
+    """The routed workload at full size through the benchmark's entry point.  "literal" poses
+    it with gains above the threshold verified as DFlash chains: W2, b2 and tau negated, every
+    sequence's layout swapped (synth.negate_second_layer)."""
+    print(f"round on routed_bf16, {polarity} polarity", flush=True)
+    batch, r = make_config("routed_bf16", polarity=polarity)
     out = _run(r, batch, dev(batch.logits), r.b2)
     _oracle(r, batch, r.b2, out)
     assert np.array_equal(out[1], batch.layout_choice) and out[2].min() >= 1
+    if polarity == "literal":
+        _, paper = make_config("routed_bf16", logits=False)
+        p_dal, p_ch = oracle.route(paper.hidden, paper.W1, paper.b1, paper.W2, paper.b2,
+                                   paper.tau, paper.dtype)
+        # chains are exactly the sequences whose paper-form gain exceeds the threshold
+        assert np.array_equal(out[1] == 0, p_dal > paper.tau)
+        assert np.all(np.abs(out[0] + p_dal) <= 1e-4 * np.maximum(1.0, np.abs(p_dal)))
 
 
 # ------------------------------------------------------------------ chain-only round
@@ -96,10 +109,25 @@ def _chain_round(r, cb, logits, b1, b2):
     assert np.array_equal(out[2], e_al) and np.array_equal(out[3], e_bo)
 
 
+@functools.lru_cache(maxsize=1)
+def _sweep_config():
+    return make_config("sweep_bf16")
+
+
 def test_round_chain_sweep_workload():
     """The 256-chain throughput-sweep workload at full size (MFMA router)."""
     print("round_chain sweep_bf16", flush=True)
-    batch, r = make_config("sweep_bf16")
+    batch, r = _sweep_config()
+    _chain_round(r, batch, dev(batch.logits), r.b1, 0.0)
+
+
+def test_round_chain_sweep_workload_paper_router_width():
+    """The same 256 chains with the paper's router width m = d/8 = 320 (WhiFlash paper,
+    Appendix A; 0.82M parameters in its Table 6) on the MFMA path: 10 hidden-unit tiles
+    of 32, the hidden size cut into 5 slices."""
+    print("round_chain sweep_bf16, router 2560 -> 320", flush=True)
+    batch, _ = _sweep_config()
+    r = make_router_inputs(4, 256, 2560, 320, "bf16")
     _chain_round(r, batch, dev(batch.logits), r.b1, 0.0)
 
 

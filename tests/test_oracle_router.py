@@ -123,3 +123,31 @@ def test_route_gather_selects_rows_and_flags_invalid():
     assert dal[0] == full[3] and dal[1] == full[0] and dal[2] == full[8] and dal[5] == full[3]
     assert np.isnan(dal[3]) and np.isnan(dal[4]) and ch[3] == 0 and ch[4] == 0
     assert ch[0] == fch[3]
+
+
+def test_negated_second_layer_flips_every_choice_off_the_band():
+    """Negating W2, b2 and tau negates the gain exactly (IEEE rounding is sign-symmetric)
+    and flips the choice of every sequence whose gain differs from tau: the routed
+    workload's literal-polarity form rests on this."""
+    from synth import negate_second_layer
+    for dtype in ("bf16", "f32"):
+        r = make_router_inputs(13, B=64, d=96, m=24, dtype=dtype, b2=1.0)
+        dal, ch = route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, dtype)
+        n = negate_second_layer(r)
+        ndal, nch = route(n.hidden, n.W1, n.b1, n.W2, n.b2, n.tau, dtype)
+        assert np.array_equal(ndal, -dal)
+        off = dal != np.float32(r.tau)
+        assert off.all() and np.array_equal(nch[off], 1 - ch[off])
+        assert 0 < ch.sum() < 64                   # both choices occur
+
+
+def test_routed_literal_layout_is_the_flipped_split():
+    from synth import make_config
+    paper, _ = make_config("routed_bf16", logits=False)
+    lit, r = make_config("routed_bf16", logits=False, polarity="literal")
+    assert np.array_equal(lit.layout_choice, 1 - paper.layout_choice)
+    dal, ch = route(r.hidden, r.W1, r.b1, r.W2, r.b2, r.tau, r.dtype)
+    assert np.array_equal(ch, lit.layout_choice)   # the negated router picks the flipped layout
+    assert np.min(np.abs(dal - r.tau)) >= 1e-3
+    sizes = np.diff(lit.offsets)
+    assert np.array_equal(sizes, np.where(lit.layout_choice == 1, 61, 17))

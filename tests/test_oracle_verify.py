@@ -254,3 +254,56 @@ def test_tree_accepted_of_a_chain_is_its_accepted_prefix():
         acc, _ = tree_accepted(t, parent, ids, d2t, V)
         al, _ = verify_chain(t[None], draft[None])
         assert acc.tolist() == [i < al[0] for i in range(K + 1)]
+
+
+# ------------------------------------------------------------------ d2t remap, exact cases
+#
+# Draft ids index a fixed 32K draft vocabulary and are mapped to target ids by
+# the d2t table before they are compared with the target's tokens (Qwen3-4B-EAGLE3
+# card, "Model Description" and "Technical Specifications").  The trees below use
+# tables far from the identity, and every expected value was derived by hand.
+# Each case also states what two wrong readings would give (comparing the draft
+# id itself, or looking the id up in the inverse table), so a mistake of either
+# kind changes AL, bonus and best node at once.
+
+
+def test_tree_d2t_reversed_table_exact():
+    V = Vd = 8
+    d2t = np.array([7, 6, 5, 4, 3, 2, 1, 0], np.int32)       # d2t[i] = 7 - i
+    parent = np.array([-1, 0, 1, 0, 3], np.int32)
+    ids = np.array([-1, 2, 6, 5, 1], np.int32)               # target ids 5, 1, 2, 6
+    t = np.array([5, 1, 4, 6, 0], np.int32)
+    # Remapped: node 1 (5 == t[0]) and node 2 (1 == t[1]) are accepted, node 3
+    # (2 != t[0]) is not, so node 4 is unreachable.  Deepest node 2 at depth 2:
+    # AL 3, bonus t[2] = 4.
+    al, bo, be = verify_tree(t[None], parent[None], ids[None], d2t, V)
+    assert (al[0], bo[0], be[0]) == (3, 4, 2)
+    # Wrong reading (no remap): node 3's raw id 5 == t[0] would win at depth 1
+    # (AL 2, bonus 6, best 3).  The table here is its own inverse, so the next
+    # case covers the inverted lookup.
+    assert (al[0], bo[0], be[0]) != (2, 6, 3)
+
+
+def test_tree_d2t_injective_into_larger_vocab_exact():
+    V, Vd = 10, 6
+    d2t = np.array([3, 0, 7, 4, 1, 8], np.int32)             # (7 i + 3) mod 10, not an involution
+    parent = np.array([-1, 0, 0, 1, 3, 2], np.int32)
+    ids = np.array([-1, 2, 0, 4, 5, 1], np.int32)            # target ids 7, 3, 1, 8, 0
+    t = np.array([7, 1, 0, 8, 2, 9], np.int32)
+    # Remapped: node 1 (7 == t[0]), node 3 (1 == t[1]) and node 4 (8 == t[3])
+    # are accepted; node 2 (3 != t[0]) is not, so node 5 is unreachable even
+    # though its target id 0 equals t[2].  Deepest node 4 at depth 3: AL 4,
+    # bonus t[4] = 2.
+    al, bo, be = verify_tree(t[None], parent[None], ids[None], d2t, V)
+    assert (al[0], bo[0], be[0]) == (4, 2, 4)
+    # No remap: raw ids 2 and 0 under the root both differ from t[0] = 7 (AL 1).
+    # Inverse lookup: id 2 is not a table entry and id 0 is entry 1 != 7 (AL 1).
+    # Through the routed dispatch, the same tree behind a chain sequence gives
+    # the same result.
+    t_rows = np.concatenate([np.array([7, 7, 7], np.int32), t])
+    offsets = np.array([0, 3, 9], np.int32)
+    choice = np.array([0, 1], np.int32)
+    chain_draft = np.array([[7, 7], [0, 0]], np.int32)
+    al, bo, be = verify_routed(t_rows, offsets, choice, 2, chain_draft, 6,
+                               np.stack([parent, parent]), np.stack([ids, ids]), d2t, V)
+    assert al.tolist() == [3, 4] and bo.tolist() == [7, 2] and be.tolist() == [2, 4]
