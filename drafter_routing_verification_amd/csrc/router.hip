@@ -39,6 +39,11 @@ constexpr int kChunksInFlight = 5;  // chunks whose loads are issued together
 // workgroups (2 slices) route 15.8 us; 512 (4 slices, two per CU, each with one
 // load batch) 15.6 us and the same step time; 1024 (7 slices) 19.0 us.
 constexpr int64_t kRouterWorkgroups = WF_ROUTER_WGS;
+// Smallest bf16 batch routed on MFMA tiles; smaller batches (and float32) take the GEMV.
+#ifndef WF_ROUTER_MFMA_MIN_BATCH
+#define WF_ROUTER_MFMA_MIN_BATCH 16
+#endif
+constexpr int32_t kMfmaMinBatch = WF_ROUTER_MFMA_MIN_BATCH;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -161,7 +166,7 @@ RouterPlan router_plan(int dtype, int32_t B, int32_t d, int32_t m, const void* h
   RouterPlan p{false, 1, d};
   const bool aligned = (reinterpret_cast<uintptr_t>(hidden) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(W1) % 16 == 0) && (d % 8 == 0);
-  if (dtype != WF_BF16 || B < 16 || !aligned) return p;
+  if (dtype != WF_BF16 || B < kMfmaMinBatch || !aligned) return p;
   p.mfma = true;
   int ks = router_max_slices(B, m);
   const int max_by_d = (d + kChunk - 1) / kChunk;
