@@ -26,6 +26,8 @@ Entry points (same names as the C ABI):
     catchup_update(cur_choice, accept_len, next_choice, backlog)  -> (switch_flag, catchup_len)
     round_chain(hidden, W1, b1, W2, b2, tau, logits, draft)   route + verify_chain fused
                  -> (delta_al, choice, accept_len, bonus, row_argmax)
+    round_chain_noalloc(hidden, W1, b1, W2, b2, tau, logits, draft)   the same, with the
+                 library's fixed device scratch in place of a workspace
     round_routed(hidden, W1, b1, W2, b2, tau, logits, row_offsets, total_rows, chain_draft,
                  parent, draft_ids, d2t)   route + verify_routed fused
                  -> (delta_al, choice, accept_len, bonus, best_node, row_argmax)
@@ -73,6 +75,8 @@ from ._binding import (  # noqa: F401
     whiflash_catchup_update,
     round_routed,
     round_chain,
+    round_chain_noalloc,
+    whiflash_round_chain_noalloc,
     round_chain_workspace_bytes,
     round_chain_early_exit,
     round_chain_early_exit_workspace_bytes,

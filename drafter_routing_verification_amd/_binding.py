@@ -65,6 +65,9 @@ _SIGNATURES = {
     "whiflash_round_chain": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_f,
                                       _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                       _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "whiflash_round_chain_noalloc": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p,
+                                              _c_f, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                              _c_i32, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "whiflash_verify_tree": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p,
                                       _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "whiflash_route_gather": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p,
@@ -187,6 +190,10 @@ def verify_routed_entropy_workspace_bytes(B: int, total_rows: int, V: int) -> in
 
 def whiflash_round_chain(*args):
     return lib().whiflash_round_chain(*args)
+
+
+def whiflash_round_chain_noalloc(*args):
+    return lib().whiflash_round_chain_noalloc(*args)
 
 
 def round_chain_workspace_bytes(B: int, m: int, K: int, V: int) -> int:
@@ -760,6 +767,40 @@ def round_chain(hidden, W1, b1, W2, b2, tau: float, logits, draft, *, row_argmax
                                 _ptr(accept_len), _ptr(bonus), _ptr(row_argmax), _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(),
                                 _stream(hidden, stream)))
+    return delta_al, choice, accept_len, bonus, row_argmax
+
+
+def round_chain_noalloc(hidden, W1, b1, W2, b2, tau: float, logits, draft, *, row_argmax=True,
+                        delta_al=None, choice=None, accept_len=None, bonus=None, stream=None):
+    """round_chain with the library's fixed device scratch instead of a workspace
+    (whiflash_round_chain_noalloc: the C call allocates nothing; outputs the caller does not
+    supply are allocated here).  Calls that overlap in time on one GPU race on the scratch."""
+    _device_tensor(hidden, "hidden")
+    B, d = hidden.shape
+    m = W1.shape[0]
+    _weights(hidden, "hidden", W1, W2)
+    if tuple(W1.shape) != (m, d) or W2.numel() != m:
+        raise ValueError("W1 must be [m, d] and W2 hold m elements")
+    dev = hidden.device
+    b1, b2 = _biases(b1, b2, m, dev)
+    _device_tensor(draft, "draft")
+    if draft.shape[0] != B:
+        raise ValueError("draft must be [B, K] with the batch of hidden")
+    K = draft.shape[1]
+    rows = B * (K + 1)
+    V, stride = _rows_view(logits, rows)
+    _i32(draft, "draft")
+    delta_al = _out(delta_al, torch.float32, B, dev, "delta_al")
+    choice = _out(choice, torch.int32, B, dev, "choice")
+    accept_len = _out(accept_len, torch.int32, B, dev, "accept_len")
+    bonus = _out(bonus, torch.int32, B, dev, "bonus")
+    row_argmax = _opt_out(row_argmax, rows, dev, "row_argmax")
+    _on(dev, logits=logits, draft=draft)
+    _check(whiflash_round_chain_noalloc(
+        _ptr(hidden), _dtype_code(hidden), d, _ptr(W1), _ptr(b1), m, _ptr(W2), _ptr(b2),
+        float(tau), _ptr(delta_al), _ptr(choice), _ptr(logits), _dtype_code(logits), B, K, V,
+        stride, _ptr(draft), _ptr(accept_len), _ptr(bonus), _ptr(row_argmax),
+        _stream(hidden, stream)))
     return delta_al, choice, accept_len, bonus, row_argmax
 
 

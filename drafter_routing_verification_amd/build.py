@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libwhiflash.so")
-SOURCES = ["api.hip", "sweep.hip", "finalize.hip", "router.hip", "entropy.hip", "catchup.hip", "round.hip", "early_exit.hip"]
+SOURCES = ["api.hip", "sweep.hip", "finalize.hip", "router.hip", "entropy.hip", "catchup.hip", "round.hip", "early_exit.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 

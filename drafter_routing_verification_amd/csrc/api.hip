@@ -53,6 +53,10 @@ const char* whiflash_status_string(int32_t status) {
     case WF_ERR_ALIGN: return "WF_ERR_ALIGN: logits base or row stride not 16-byte aligned";
     case WF_ERR_WORKSPACE: return "WF_ERR_WORKSPACE: workspace NULL, not 256-byte aligned, or too small";
     case WF_ERR_LAUNCH: return "WF_ERR_LAUNCH: kernel launch failed";
+    case WF_ERR_SCRATCH:
+      return "WF_ERR_SCRATCH: the round needs more than the fixed scratch of the "
+             "no-allocation entry point";
+    case WF_ERR_RUNTIME: return "WF_ERR_RUNTIME: a HIP runtime query failed";
     default: return "unknown whiflash status";
   }
 }
@@ -576,13 +580,16 @@ size_t whiflash_round_chain_workspace_bytes(int32_t B, int32_t m, int32_t K, int
          whiflash_verify_workspace_bytes(static_cast<int32_t>(rows), V);
 }
 
-int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
-                             const float* b1, int32_t m, const void* W2, const float* b2,
-                             float tau, float* delta_al, int32_t* choice, const void* logits,
-                             int32_t logits_dtype, int32_t B, int32_t K, int32_t V,
-                             int64_t row_stride, const int32_t* draft, int32_t* accept_len,
-                             int32_t* bonus, int32_t* row_argmax, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace wf {
+
+// Every check of whiflash_round_chain's arguments except the workspace's.
+int32_t round_chain_check(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
+                          int32_t m, const void* W2, const float* delta_al, const int32_t* choice,
+                          const void* logits, int32_t logits_dtype, int32_t B, int32_t K, int32_t V,
+                          int64_t row_stride, const int32_t* draft, const int32_t* accept_len,
+                          const int32_t* bonus) {
   // Router arguments, as whiflash_route.
   if (!valid_dtype(hidden_dtype)) return WF_ERR_DTYPE;
   if (B < 0 || d <= 0 || m <= 0) return WF_ERR_SHAPE;
@@ -590,15 +597,32 @@ int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d
   if (K < 0 || K >= WHIFLASH_MAX_SEQ_ROWS) return WF_ERR_SHAPE;
   const int64_t rows64 = static_cast<int64_t>(B) * (K + 1);
   if (rows64 > INT32_MAX) return WF_ERR_SHAPE;
-  const int32_t rows = static_cast<int32_t>(rows64);
-  int32_t s = check_logits(logits, logits_dtype, rows, V, row_stride);
+  const int32_t s = check_logits(logits, logits_dtype, static_cast<int32_t>(rows64), V, row_stride);
   if (s != WF_OK) return s;
   if (B == 0) return WF_OK;
   if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
   if (!accept_len || !bonus || (K > 0 && !draft)) return WF_ERR_NULL;
-  if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
+  if (static_cast<int64_t>(B) * m * kMaxRouterSlices > INT32_MAX ||
       static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
     return WF_ERR_SHAPE;
+  return WF_OK;
+}
+
+}  // namespace wf
+
+extern "C" {
+
+int32_t whiflash_round_chain(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
+                             const float* b1, int32_t m, const void* W2, const float* b2,
+                             float tau, float* delta_al, int32_t* choice, const void* logits,
+                             int32_t logits_dtype, int32_t B, int32_t K, int32_t V,
+                             int64_t row_stride, const int32_t* draft, int32_t* accept_len,
+                             int32_t* bonus, int32_t* row_argmax, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  int32_t s = wf::round_chain_check(hidden, hidden_dtype, d, W1, m, W2, delta_al, choice, logits,
+                                    logits_dtype, B, K, V, row_stride, draft, accept_len, bonus);
+  if (s != WF_OK || B == 0) return s;
+  const int32_t rows = B * (K + 1);
   if ((s = check_workspace(workspace, workspace_bytes,
                            whiflash_round_chain_workspace_bytes(B, m, K, V))) != WF_OK)
     return s;

@@ -133,6 +133,14 @@ hipError_t launch_early_exit_round(const void* logits, int dtype, int64_t row_st
                                    float* delta_al, int32_t* choice, int32_t* accept_len,
                                    int32_t* bonus, int32_t* row_argmax, hipStream_t stream);
 
+// Every check of whiflash_round_chain's arguments except the workspace's (WF_OK or a
+// negative status; runs no HIP call).
+int32_t round_chain_check(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
+                          int32_t m, const void* W2, const float* delta_al, const int32_t* choice,
+                          const void* logits, int32_t logits_dtype, int32_t B, int32_t K, int32_t V,
+                          int64_t row_stride, const int32_t* draft, const int32_t* accept_len,
+                          const int32_t* bonus);
+
 hipError_t launch_finalize_chain(const Partial* part, int32_t splits, int32_t B, int32_t K,
                                  const int32_t* draft, int32_t* accept_len, int32_t* bonus,
                                  int32_t* row_argmax, hipStream_t stream);

@@ -17,7 +17,8 @@
  *
  * Conventions shared by every entry point:
  *   - Every array argument is a DEVICE pointer owned by the caller.  The
- *     library keeps no pointer after the call returns and holds no state.
+ *     library keeps no pointer after the call returns and holds no state,
+ *     apart from the fixed scratch of whiflash_round_chain_noalloc.
  *   - Calls are asynchronous on `stream` (0 = the default stream); none
  *     synchronises and none allocates.  Scratch memory comes from the
  *     caller's `workspace` (device memory of at least the size returned by
@@ -55,7 +56,9 @@ typedef enum {
   WF_ERR_DTYPE = -3,     /* dtype is not a wf_dtype value                    */
   WF_ERR_ALIGN = -4,     /* logits base or row stride not 16-byte aligned    */
   WF_ERR_WORKSPACE = -5, /* workspace NULL, misaligned or smaller than needed */
-  WF_ERR_LAUNCH = -6     /* the HIP runtime rejected a kernel launch         */
+  WF_ERR_LAUNCH = -6,    /* the HIP runtime rejected a kernel launch         */
+  WF_ERR_SCRATCH = -7,   /* the call needs more than the fixed scratch holds  */
+  WF_ERR_RUNTIME = -8    /* a HIP runtime query (device, symbol) failed       */
 } wf_status;
 
 /* Largest K+1 (chain) or N (tree) rows per sequence the kernels accept. */
@@ -478,6 +481,37 @@ int32_t whiflash_round_chain_early_exit(const void* hidden, int32_t hidden_dtype
                                         const int32_t* draft, int32_t* accept_len, int32_t* bonus,
                                         int32_t* row_argmax, void* workspace,
                                         size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the fixed device scratch of whiflash_round_chain_noalloc (per GPU). */
+#define WHIFLASH_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * whiflash_round_chain for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, layouts, results and error codes are those of whiflash_round_chain,
+ * without the workspace: the round's scratch is a fixed array of
+ * WHIFLASH_NOALLOC_SCRATCH_BYTES bytes of device memory inside the library, one
+ * copy per GPU, held until the process ends.  The call allocates nothing.
+ *   - A round whose whiflash_round_chain_workspace_bytes(B, m, K, V) exceeds
+ *     WHIFLASH_NOALLOC_SCRATCH_BYTES returns WF_ERR_SCRATCH and launches
+ *     nothing (about 1,400 sequences at K = 16, V = 151,936, m = 1024; 256
+ *     sequences need 2.4 MB).
+ *   - The GPU is the stream's device (the current device for stream 0).  The
+ *     first call on each GPU looks up that GPU's address of the array
+ *     (WF_ERR_RUNTIME if the runtime cannot give it); later calls reuse it.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents.  Calls that overlap in time on one GPU (different
+ *     streams, or host threads) race on it and must be serialised by the
+ *     caller.  Nothing in it needs clearing: each call writes every byte it
+ *     reads before reading it.
+ */
+int32_t whiflash_round_chain_noalloc(const void* hidden, int32_t hidden_dtype, int32_t d,
+                                     const void* W1, const float* b1, int32_t m, const void* W2,
+                                     const float* b2, float tau, float* delta_al, int32_t* choice,
+                                     const void* logits, int32_t logits_dtype, int32_t B,
+                                     int32_t K, int32_t V, int64_t row_stride,
+                                     const int32_t* draft, int32_t* accept_len, int32_t* bonus,
+                                     int32_t* row_argmax, hipStream_t stream);
 
 #ifdef __cplusplus
 }

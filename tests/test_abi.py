@@ -28,7 +28,7 @@ def test_header_symbols_exported():
 
 
 def test_status_strings():
-    for code in range(-6, 1):
+    for code in range(-8, 1):
         s = wf.status_string(code)
         assert s.startswith("WF_") and s != "unknown whiflash status"
     assert wf.status_string(5) == "unknown whiflash status"
@@ -245,3 +245,27 @@ def test_workspace_queries_reject_row_counts_past_int32():
     # Just inside the limit the queries still answer.
     assert wf.early_exit_workspace_bytes(2**21 - 1, 1023, V) > 0
     assert wf.tree_early_exit_workspace_bytes(2**21 - 1, 1024, V) > 0
+
+
+def test_round_chain_noalloc_validation():
+    """Argument checks of whiflash_round_chain_noalloc, all before any HIP call: those of
+    whiflash_round_chain, then the fixed scratch's limit."""
+    f = wf.whiflash_round_chain_noalloc
+    A = ALIGNED
+    # (hidden, hdt, d, W1, b1, m, W2, b2, tau, dal, choice, logits, ldt, B, K, V, stride, draft,
+    #  al, bonus, rows, stream)
+    ok = [A, 1, 2560, A, None, 1024, A, None, 1.0, A, A, A, 1, 256, 16, V, V, A, A, A, None, None]
+    big = list(ok); big[13] = 1600                 # 1,600 chains need more than 8 MiB
+    assert wf.round_chain_workspace_bytes(1600, 1024, 16, V) > (8 << 20)
+    assert wf.round_chain_workspace_bytes(256, 1024, 16, V) <= (8 << 20)
+    assert f(*big) == -7 and "scratch" in wf.status_string(-7)
+    bad = list(big); bad[0] = None
+    assert f(*bad) == -1                           # argument errors come first
+    bad = list(ok); bad[12] = 5
+    assert f(*bad) == -3
+    bad = list(ok); bad[14] = 1024
+    assert f(*bad) == -2
+    bad = list(ok); bad[11] = A + 2
+    assert f(*bad) == -4
+    zero = list(ok); zero[13] = 0
+    assert f(*zero) == 0                           # B = 0: no-op
