@@ -167,10 +167,11 @@ def test_round_chain_batched_chain_config():
     _chain_round(r, batch, dev(batch.logits), r.b1, 0.0)
 
 
-@pytest.mark.parametrize("B", [12, 16, 24, 32, 33])
+@pytest.mark.parametrize("B", [9, 10, 12, 15, 16, 24, 32, 33])
 def test_round_chain_mid_batches(B):
-    """12 to 33 sequences on 16-byte aligned operands, around the MFMA router's 16-sequence
-    switch (the GEMV router below it, two launches per round from 9 sequences on)."""
+    """9 to 33 sequences on 16-byte aligned operands, around the MFMA router's 10-sequence
+    switch (the GEMV router below it; two launches per round up to 8 sequences, three from
+    9 on)."""
     from synth import make_chain_batch
     print(f"round_chain batch tiles B={B}", flush=True)
     r = make_router_inputs(B + 500, B, 2560, 1024, "bf16")
