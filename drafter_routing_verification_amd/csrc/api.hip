@@ -29,6 +29,8 @@ int32_t check_workspace(void* ws, size_t have, size_t need) {
 int32_t check_logits(const void* logits, int32_t dtype, int32_t rows, int32_t V, int64_t row_stride) {
   if (!valid_dtype(dtype)) return WF_ERR_DTYPE;
   if (V <= 0 || rows < 0 || row_stride < V) return WF_ERR_SHAPE;
+  // The byte offset of every row, rows * row_stride * element size, must fit in int64.
+  if (row_stride > INT64_MAX / 16 / (rows > 0 ? rows : 1)) return WF_ERR_SHAPE;
   if (rows > 0 && logits == nullptr) return WF_ERR_NULL;
   if (!aligned16(logits) || (row_stride * elem_bytes(dtype)) % 16 != 0) return WF_ERR_ALIGN;
   const wf::SweepPlan plan = wf::sweep_plan(rows, V);
@@ -120,7 +122,8 @@ int32_t route_impl(const void* hidden, const wf::HiddenSel& sel, int32_t dtype, 
   if (B == 0) return WF_OK;
   if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
   if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
-      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535 ||
+      d > wf::kMaxHidden)
     return WF_ERR_SHAPE;
   const int32_t s = check_workspace(workspace, workspace_bytes, whiflash_route_workspace_bytes(B, m));
   if (s != WF_OK) return s;
@@ -318,7 +321,8 @@ int32_t whiflash_round_routed(const void* hidden, int32_t hidden_dtype, int32_t 
       !bonus)
     return WF_ERR_NULL;
   if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
-      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535 ||
+      d > wf::kMaxHidden)
     return WF_ERR_SHAPE;
   const size_t route_bytes = whiflash_route_workspace_bytes(B, m);
   if ((s = check_workspace(workspace, workspace_bytes,
@@ -501,7 +505,8 @@ int32_t whiflash_round_routed_early_exit(
       !bonus)
     return WF_ERR_NULL;
   if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
-      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535 ||
+      d > wf::kMaxHidden)
     return WF_ERR_SHAPE;
   if (!ee_grid_ok(B, K + 1 > N ? K + 1 : N, V)) return WF_ERR_SHAPE;
   if ((s = check_workspace(workspace, workspace_bytes,
@@ -603,7 +608,8 @@ int32_t round_chain_check(const void* hidden, int32_t hidden_dtype, int32_t d, c
   if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
   if (!accept_len || !bonus || (K > 0 && !draft)) return WF_ERR_NULL;
   if (static_cast<int64_t>(B) * m * kMaxRouterSlices > INT32_MAX ||
-      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535 ||
+      d > wf::kMaxHidden)
     return WF_ERR_SHAPE;
   return WF_OK;
 }
@@ -667,7 +673,8 @@ int32_t whiflash_round_chain_early_exit(const void* hidden, int32_t hidden_dtype
   if (!hidden || !W1 || !W2 || !delta_al || !choice) return WF_ERR_NULL;
   if (!accept_len || !bonus || (K > 0 && !draft)) return WF_ERR_NULL;
   if (static_cast<int64_t>(B) * m * wf::kMaxRouterSlices > INT32_MAX ||
-      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535)
+      static_cast<int64_t>(m) * d > (int64_t{1} << 40) || B > 65535 ||
+      d > wf::kMaxHidden)
     return WF_ERR_SHAPE;
   const wf::SweepPlan plan = wf::early_exit_plan(B, V);
   if (rows64 * plan.splits * 1024 >= (int64_t{1} << 32)) return WF_ERR_SHAPE;

@@ -12,6 +12,8 @@ constexpr int kThreads = 256;          // every kernel runs 256-thread workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxSeqRows = WHIFLASH_MAX_SEQ_ROWS;
 constexpr int kRowsPerThread = kMaxSeqRows / kThreads;
+// Largest router hidden size (keeps every column index of a hidden row far inside int).
+constexpr int32_t kMaxHidden = WHIFLASH_MAX_HIDDEN;
 
 // Partial result of the argmax sweep over one chunk of one row: the chunk's
 // maximum and the lowest index holding it.

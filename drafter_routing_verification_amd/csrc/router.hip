@@ -173,19 +173,21 @@ RouterPlan router_plan(int dtype, int32_t B, int32_t d, int32_t m, const void* h
                        (reinterpret_cast<uintptr_t>(W1) % 16 == 0) && (d % 8 == 0);
   if (dtype != WF_BF16 || B < kMfmaMinBatch || !aligned) return p;
   p.mfma = true;
-  int ks = router_max_slices(B, m);
-  const int max_by_d = (d + kChunk - 1) / kChunk;
+  // 64-bit arithmetic: d may come close to INT32_MAX.
+  int64_t ks = router_max_slices(B, m);
+  const int64_t max_by_d = (static_cast<int64_t>(d) + kChunk - 1) / kChunk;
   if (ks > max_by_d) ks = max_by_d;
-  const int per = (d + ks - 1) / ks;
-  p.kslice = (per + kChunk - 1) / kChunk * kChunk;
-  p.slices = (d + p.kslice - 1) / p.kslice;
+  const int64_t per = (static_cast<int64_t>(d) + ks - 1) / ks;
+  const int64_t kslice = (per + kChunk - 1) / kChunk * kChunk;
+  p.kslice = static_cast<int32_t>(kslice < d ? kslice : d);
+  p.slices = static_cast<int32_t>((static_cast<int64_t>(d) + kslice - 1) / kslice);
   return p;
 }
 
 int32_t router_max_slices(int32_t B, int32_t m) {
   // Split the hidden size until the grid covers ~kRouterWorkgroups workgroups.
-  const int64_t tiles = static_cast<int64_t>((m + kMfmaTileJ - 1) / kMfmaTileJ) *
-                        ((B + kMfmaTileB - 1) / kMfmaTileB);
+  const int64_t tiles = ((static_cast<int64_t>(m) + kMfmaTileJ - 1) / kMfmaTileJ) *
+                        ((static_cast<int64_t>(B) + kMfmaTileB - 1) / kMfmaTileB);
   int64_t ks = tiles > 0 ? kRouterWorkgroups / tiles : 1;
   if (ks < 1) ks = 1;
   if (ks > kMaxRouterSlices) ks = kMaxRouterSlices;

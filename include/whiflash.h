@@ -64,6 +64,9 @@ typedef enum {
 /* Largest K+1 (chain) or N (tree) rows per sequence the kernels accept. */
 #define WHIFLASH_MAX_SEQ_ROWS 1024
 
+/* Largest router hidden size d (and at most 65,535 sequences per router call). */
+#define WHIFLASH_MAX_HIDDEN (1 << 24)
+
 /* Human-readable name of a wf_status value (static string; host only). */
 const char* whiflash_status_string(int32_t status);
 
@@ -130,7 +133,8 @@ int32_t whiflash_stream_read(const void* logits, int32_t dtype, int32_t rows, in
  *   b1 [m] float32 or NULL (= 0); b2: pointer to one float32 or NULL (= 0).
  *   Accumulation, GELU and the second layer run in float32.
  *   delta_al [B] float32 and choice [B] int32 are written.
- * B == 0 is a no-op. d, m >= 1.  The paper's router uses m = d/8; any m works.
+ * B == 0 is a no-op.  1 <= d <= WHIFLASH_MAX_HIDDEN, m >= 1, B <= 65535.  The
+ * paper's router uses m = d/8; any m works.
  */
 int32_t whiflash_route(const void* hidden, int32_t dtype, int32_t B, int32_t d,
                        const void* W1, const float* b1, int32_t m,
