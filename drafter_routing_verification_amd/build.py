@@ -30,7 +30,9 @@ def command(out: str) -> list[str]:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Wall", "-Wno-unused-command-line-argument",
-        # packed fp32 VALU ops stay off (see the build notes in the package docstring)
+        # no packed fp32 VALU instructions (v_pk_add/mul/fma_f32): the compiler would
+        # otherwise pair the kernels' scalar float32 operations into them; all float
+        # arithmetic here is meant to run as scalar float32 VALU instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE, "-I", CSRC, "-o", out,
     ] + [os.path.join(CSRC, s) for s in SOURCES]
