@@ -30,6 +30,9 @@ struct SweepPlan {
 };
 
 SweepPlan sweep_plan(int32_t rows, int32_t V);
+// Whether a sweep launch of `blocks` workgroups issues each thread's whole batch of
+// loads at once (small launches) or one load at a time.
+bool sweep_batched(int64_t blocks);
 
 // Row of sequence b selected as row0[b] + pos[b] (row0 NULL: b * rows_per_seq),
 // or -1 when pos[b] < 0 or the row falls outside [0, total_rows).

@@ -12,8 +12,30 @@
 #include "accept.h"
 #include "common.h"
 #include "gemv_body.h"
+#include "interleave.h"
 #include "router_math.h"
+#include "router_tile.h"
 #include "sweep_body.h"
+
+// Router tiles of a shared launch sit within the first WF_ROUTER_INTERLEAVE
+// percent of each XCD's workgroups (0: router stage 1 always gets a launch of
+// its own).  Only a router of at most WF_ROUTER_INTERLEAVE_LOADS chunk loads
+// (tiles x 64-column chunks per tile) shares the sweep's launch.
+//
+// Same box, bench step, two interleaved trials, separate launch -> shared launch
+// (first 25 / 50 / 75 / 100 percent):
+//   32 chains, 2560 -> 1024 (224 tiles x 6 chunks)   35.1 -> 31.0 / 31.2 / 32.5 / 33.0 us
+//   128 routed, 2560 -> 1024 (256 tiles x 10 chunks)  220.1 -> 221.9 / 223.0 / 224.4 / 226.4 us
+//   256 chains, 2560 -> 1024 (256 tiles x 20 chunks)  197.5 -> 203.4 / 202.7 / 202.1 / 213.3 us
+// Under a sweep that saturates HBM every chunk a tile loads is a long round
+// trip, and a tile holds its slot for all of them: a large router costs the
+// sweep more than its own launch does.
+#ifndef WF_ROUTER_INTERLEAVE
+#define WF_ROUTER_INTERLEAVE 25
+#endif
+#ifndef WF_ROUTER_INTERLEAVE_LOADS
+#define WF_ROUTER_INTERLEAVE_LOADS 2048
+#endif
 
 namespace wf {
 namespace {
@@ -98,6 +120,27 @@ __global__ __launch_bounds__(kThreads) void router_sweep_kernel(
   }
 }
 
+// First launch of a round on the MFMA router path: router stage-1 tiles (lean
+// form, router_tile.h) spaced through the first part of every XCD's workgroups,
+// the sweep's chunks in all other positions (interleave.h).  The two kinds read
+// disjoint inputs and write disjoint outputs.
+template <int DTL, bool kBatch>
+__global__ __launch_bounds__(kThreads) void router_mfma_sweep_kernel(
+    const unsigned short* __restrict__ hidden, int B, int d, const unsigned short* __restrict__ W1,
+    int m, int kslice, int KS, int tiles_j, int tiles_b, float* __restrict__ zp,
+    int64_t router_per_xcd, int64_t spacing, const unsigned char* __restrict__ logits,
+    int64_t row_bytes, int V, int splits, int chunk_vecs, int nvec, Partial* __restrict__ part) {
+  __shared__ LeanStage stage;
+  const int64_t t = interleave_map(blockIdx.x, gridDim.x, router_per_xcd, spacing);
+  if (t < 0) {
+    router_lean_tile(static_cast<int>(-t - 1), tiles_j, tiles_b, KS, hidden, B, d, W1, m, kslice,
+                     zp, stage);
+  } else {
+    sweep_chunk<DTL, kThreads, kBatch>(static_cast<int>(t), logits, row_bytes, V, splits,
+                                       chunk_vecs, nvec, part);
+  }
+}
+
 template <int DTL, int DTH>
 hipError_t launch_router_sweep_nb(unsigned grid, int nb, const void* hidden, int B, int d,
                                   const void* W1, int m, float* zp, int router_blocks,
@@ -144,6 +187,37 @@ SweepPlan few_rows_plan(int32_t rows, int32_t V, int32_t rows_per_seq) {
   return p;
 }
 
+namespace {
+
+// Router stage 1 (MFMA path) and the sweep in one launch, tiles interleaved.
+template <int DTL>
+hipError_t launch_router_mfma_sweep(const RouterPlan& plan, const void* hidden, int32_t B, int32_t d,
+                                    const void* W1, int32_t m, float* zp, const void* logits,
+                                    int64_t row_stride, int32_t rows, int32_t V, SweepPlan sp,
+                                    Partial* part, int64_t r, hipStream_t stream) {
+  using E = Elem<DTL>;
+  const int tiles_j = (m + kTileJ - 1) / kTileJ, tiles_b = (B + kTileB - 1) / kTileB;
+  const int64_t sweep_blocks = static_cast<int64_t>(rows) * sp.splits;
+  const int64_t n = sweep_blocks + kXcdCount * r;
+  const int64_t s = interleave_spacing(n, r, WF_ROUTER_INTERLEAVE);
+  const unsigned char* base = static_cast<const unsigned char*>(logits);
+  const int64_t rb = row_stride * E::kBytes;
+  const int cv = sp.chunk / E::kPerVec, nv = V / E::kPerVec;
+  const unsigned short* h = static_cast<const unsigned short*>(hidden);
+  const unsigned short* w = static_cast<const unsigned short*>(W1);
+  if (sweep_batched(sweep_blocks))
+    hipLaunchKernelGGL((router_mfma_sweep_kernel<DTL, true>), dim3(static_cast<unsigned>(n)),
+                       dim3(kThreads), 0, stream, h, B, d, w, m, plan.kslice, plan.slices, tiles_j,
+                       tiles_b, zp, r, s, base, rb, V, sp.splits, cv, nv, part);
+  else
+    hipLaunchKernelGGL((router_mfma_sweep_kernel<DTL, false>), dim3(static_cast<unsigned>(n)),
+                       dim3(kThreads), 0, stream, h, B, d, w, m, plan.kslice, plan.slices, tiles_j,
+                       tiles_b, zp, r, s, base, rb, V, sp.splits, cv, nv, part);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_round_stage1(bool fused, const RouterPlan& plan, int hidden_dtype,
                                const void* hidden, int32_t B, int32_t d, const void* W1, int32_t m,
                                float* zp, const void* logits, int logits_dtype, int64_t row_stride,
@@ -151,6 +225,21 @@ hipError_t launch_round_stage1(bool fused, const RouterPlan& plan, int hidden_dt
                                hipStream_t stream) {
   const int64_t router_gx = (static_cast<int64_t>(m) + kWaves - 1) / kWaves;
   const int64_t sweep_blocks = static_cast<int64_t>(rows) * sp.splits;
+  if (WF_ROUTER_INTERLEAVE > 0 && plan.mfma && plan.kslice % kLeanChunk == 0) {
+    // Router tiles padded to a whole number per XCD; the padding tiles do nothing.
+    const int64_t tiles = static_cast<int64_t>((m + kTileJ - 1) / kTileJ) *
+                          ((B + kTileB - 1) / kTileB) * plan.slices;
+    const int64_t loads = tiles * (plan.kslice / kLeanChunk);
+    const int64_t r = (tiles + kXcdCount - 1) / kXcdCount;
+    if (loads <= WF_ROUTER_INTERLEAVE_LOADS && sweep_blocks + kXcdCount * r <= INT32_MAX &&
+        sweep_blocks / kXcdCount >= r) {
+      return logits_dtype == WF_BF16
+                 ? launch_router_mfma_sweep<WF_BF16>(plan, hidden, B, d, W1, m, zp, logits,
+                                                     row_stride, rows, V, sp, part, r, stream)
+                 : launch_router_mfma_sweep<WF_F32>(plan, hidden, B, d, W1, m, zp, logits,
+                                                    row_stride, rows, V, sp, part, r, stream);
+    }
+  }
   if (!fused || router_gx + sweep_blocks > INT32_MAX) {
     const HiddenSel direct{nullptr, nullptr, 0, 0};
     if (launch_router_stage1(plan, hidden, direct, hidden_dtype, B, d, W1, m, zp, stream) !=

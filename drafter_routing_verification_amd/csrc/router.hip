@@ -173,13 +173,13 @@ RouterPlan router_plan(int dtype, int32_t B, int32_t d, int32_t m, const void* h
                        (reinterpret_cast<uintptr_t>(W1) % 16 == 0) && (d % 8 == 0);
   if (dtype != WF_BF16 || B < kMfmaMinBatch || !aligned) return p;
   p.mfma = true;
-  // 64-bit arithmetic: d may come close to INT32_MAX.
+  // 64-bit arithmetic: the slice width is d rounded up to a multiple of kChunk.
   int64_t ks = router_max_slices(B, m);
   const int64_t max_by_d = (static_cast<int64_t>(d) + kChunk - 1) / kChunk;
   if (ks > max_by_d) ks = max_by_d;
   const int64_t per = (static_cast<int64_t>(d) + ks - 1) / ks;
   const int64_t kslice = (per + kChunk - 1) / kChunk * kChunk;
-  p.kslice = static_cast<int32_t>(kslice < d ? kslice : d);
+  p.kslice = static_cast<int32_t>(kslice);
   p.slices = static_cast<int32_t>((static_cast<int64_t>(d) + kslice - 1) / kslice);
   return p;
 }

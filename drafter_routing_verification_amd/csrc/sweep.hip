@@ -8,7 +8,7 @@
 #define WF_SWEEP_THREADS 256
 #endif
 #ifndef WF_SWEEP_CHUNK
-#define WF_SWEEP_CHUNK 14400
+#define WF_SWEEP_CHUNK 10000
 #endif
 
 namespace wf {
@@ -101,12 +101,26 @@ __global__ __launch_bounds__(kSweepThreads) void stream_read_kernel(
 
 }  // namespace
 
+bool sweep_batched(int64_t blocks) { return blocks <= kSmallLaunch; }
+
 SweepPlan sweep_plan(int32_t rows, int32_t V) {
-  // 256-thread workgroups over chunks of ~14.4K elements (~28 KB of bf16),
-  // rounded down to an odd count per row: 11 per 151,936-wide row (13,824
-  // elements) and 9 per 128,256-wide row (14,336).  Small batches split
-  // further so a launch still has about 2048 workgroups, but never below 2048
-  // elements per chunk.
+  // 256-thread workgroups over chunks of ~10K elements (~20 KB of bf16),
+  // rounded down to an odd count per row: 15 per 151,936-wide row (10,240
+  // elements: 5 loads of 16 bytes per thread) and 13 per 128,256-wide row.
+  // Small batches split further so a launch still has about 2048 workgroups,
+  // but never below 2048 elements per chunk.
+  //
+  // Same box, bench line on the 256-chain and routed workloads, two interleaved
+  // trials each, sweep kernel alone (whole step):
+  //   11 chunks per row (13,824)  184.2-184.3 us (199.9-200.3)   routed 209.3 (223.4-223.5)
+  //   13 chunks (11,776)          183.3-183.4 us (198.9-199.1)   routed 208.3-208.7 (221.9-222.3)
+  //   15 chunks (10,240)          182.2 us (198.1-198.3)         routed 207.7-207.9 (221.0-221.3)
+  //   17 chunks (9,216)           187.7-188.0 us (203.9-204.0)   routed 213.7 (228.0-228.1)
+  //   19 chunks (8,192)           192.6-192.8 us (208.7-208.9)   routed 216.7-216.8 (232.1-232.4)
+  // The same change moved the 32-chain and 8-tree sweeps by -0.2 us, the
+  // Llama-shape sweep (9 -> 13 chunks) within its spread, the one-sequence round
+  // not at all.  Earlier, with the XCD-contiguous numbering and the 12.8K-14.4K
+  // targets:
   //
   // Same-box A/B on the Llama-shape chain workload (2,816 x 128,256 rows, three
   // interleaved trials): 9 chunks per row (this target) 104.96-105.31 us for

@@ -16,6 +16,7 @@
 #include <string>
 #include <vector>
 
+#include "interleave.h"
 #include "whiflash.h"
 
 // ----------------------------------------------------------------------------- HIP stand-ins
@@ -196,7 +197,7 @@ void calls() {
   };
   const Shape shapes[] = {{1, 16, 61, 2560, 1024, WF_F32}, {5, 16, 61, 256, 64, WF_BF16},
                           {9, 0, 1, 96, 50, WF_BF16},      {32, 16, 61, 2560, 1024, WF_BF16},
-                          {256, 16, 61, 2560, 320, WF_BF16}, {300, 1023, 1024, 104, 70, WF_BF16}};
+                          {256, 16, 61, 2560, 320, WF_BF16}, {250, 1023, 1024, 104, 70, WF_BF16}};
   for (const Shape& s : shapes) {
     const int32_t crow = s.B * (s.K + 1), trow = s.B * s.N;
     char tag[96];
@@ -347,9 +348,55 @@ void rejections() {
   for (int32_t s = -9; s <= 1; ++s) EXPECT(whiflash_status_string(s) != nullptr, "status string");
 }
 
+// The interleaved numbering of a shared router + sweep launch (interleave.h) is a
+// bijection onto the sweep's chunks and the router tiles, every XCD sweeps one
+// contiguous range of chunks in increasing order, and every XCD runs r tiles.
+void interleave_bijection() {
+  const int64_t sweeps[] = {1, 7, 8, 9, 100, 2176, 5368, 5984, 8160, 47872, 65280, 74880};
+  const int64_t routers[] = {1, 2, 3, 16, 32, 64, 128, 257};
+  const int percents[] = {1, 25, 50, 75, 100};
+  for (int64_t S : sweeps)
+    for (int64_t r : routers)
+      for (int pct : percents) {
+        if (S / 8 < r) continue;  // the launch path requires a full set of router positions
+        const int64_t n = S + 8 * r;
+        const int64_t sp = wf::interleave_spacing(n, r, pct);
+        char tag[96];
+        snprintf(tag, sizeof tag, "interleave S=%lld r=%lld pct=%d", (long long)S, (long long)r, pct);
+        EXPECT(sp >= 1 && r * sp <= n / 8, tag);
+        std::vector<char> chunk(S, 0), tile(8 * r, 0);
+        std::vector<int64_t> last(8, -1), lo(8, INT64_MAX), hi(8, -1), tiles_on(8, 0);
+        for (int64_t i = 0; i < n; ++i) {
+          const int64_t t = wf::interleave_map(i, n, r, sp);
+          const int x = static_cast<int>(i % 8);
+          if (t >= 0) {
+            EXPECT(t < S && !chunk[t], tag);
+            if (t < S) chunk[t] = 1;
+            EXPECT(t > last[x], tag);  // increasing along the XCD's positions
+            last[x] = t;
+            lo[x] = t < lo[x] ? t : lo[x];
+            hi[x] = t > hi[x] ? t : hi[x];
+          } else {
+            const int64_t u = -t - 1;
+            EXPECT(u < 8 * r && !tile[u] && u / r == x, tag);
+            if (u < 8 * r) tile[u] = 1;
+            ++tiles_on[x];
+          }
+        }
+        int64_t covered = 0;
+        for (int x = 0; x < 8; ++x) {
+          EXPECT(tiles_on[x] == r, tag);
+          if (hi[x] >= 0) covered += hi[x] - lo[x] + 1;
+          if (x > 0 && hi[x] >= 0 && hi[x - 1] >= 0) EXPECT(lo[x] == hi[x - 1] + 1, tag);
+        }
+        EXPECT(covered == S, tag);  // contiguous per XCD, no gaps or overlaps
+      }
+}
+
 }  // namespace
 
 int main() {
+  interleave_bijection();
   plans();
   workspace_sizes();
   calls();

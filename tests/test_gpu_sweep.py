@@ -96,7 +96,7 @@ def test_sweep_workload_full_size():
     batch, _ = make_config("sweep_bf16")
     logits = dev(batch.logits)
     vals, idx = (host(t) for t in wf.argmax_sweep(logits))
-    assert vals.shape[1] == 11
+    assert vals.shape[1] == wf.argmax_sweep_plan(batch.rows, batch.V)[0] == 15
     t = oracle.row_argmax(batch.logits, "bf16")
     assert np.array_equal(_merged(vals, idx), t)
     sample = np.random.default_rng(11).choice(batch.rows, 24, replace=False)

@@ -57,7 +57,7 @@ def test_abi_host_code_under_asan_and_ubsan(tmp_path):
     stub = tmp_path / "fatbin_stubs.c"
     stub.write_text("".join(f"char {b}[16] __attribute__((aligned(16)));\n" for b in blobs))
     drv = str(tmp_path / "abi_driver.o")
-    _run([CLANG, "-O1", "-g", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+    _run([CLANG, "-O1", "-g", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", CSRC,
           "-I", os.path.join(ROCM, "include"), *SANITIZE, "-c", DRIVER, "-o", drv])
     exe = str(tmp_path / "abi_driver")
     _run([CLANG, *SANITIZE, "-x", "c", str(stub), "-x", "none", drv, *objs, "-o", exe,
