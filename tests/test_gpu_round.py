@@ -181,6 +181,31 @@ def test_round_chain_mid_batches(B):
     _chain_round(r, cb, padded_logits(cb.logits, (V + 7) // 8 * 8 + 8), b1, 0.0)
 
 
+@pytest.mark.parametrize("B,ldt,V", [(20, "f32", 20011), (64, "bf16", 30011), (65, "bf16", 30011),
+                                      (11, "bf16", 151936)])
+def test_round_chain_shared_launch(B, ldt, V):
+    """bf16 routers small enough to run their tiles inside the sweep's launch (10 to 64
+    sequences on one tile row; 65 spans two and keeps a launch of its own), with float32
+    or bf16 logits, ragged and full-width vocabularies."""
+    from synth import make_chain_batch
+    print(f"round_chain shared launch B={B} logits={ldt} V={V}", flush=True)
+    r = make_router_inputs(B + 700, B, 2560, 1024, "bf16")
+    b1 = (np.random.default_rng(B + 3).standard_normal(r.m) * 0.5).astype(np.float32)
+    cb = make_chain_batch(B + 701, B, 16, V, ldt)
+    _chain_round(r, cb, padded_logits(cb.logits, (V + 7) // 8 * 8 + 8), b1, 0.0)
+
+
+def test_round_routed_shared_launch():
+    """A routed round of 40 sequences (router tiles inside the sweep's launch), mixed chains and
+    trees over the full vocabulary."""
+    print("round_routed shared launch B=40", flush=True)
+    r = make_router_inputs(740, 40, 2560, 1024, "bf16")
+    layout = np.random.default_rng(40).integers(0, 2, 40).astype(np.int32)
+    rb = make_routed_batch(741, layout, K=16, N=61, V=151936, Vd=32000, dtype="bf16")
+    out = _run(r, rb, dev(rb.logits), 0.0)
+    _oracle(r, rb, 0.0, out)
+
+
 def test_round_chain_single_sequence_f32():
     """The single-sequence float32 workload at full size: K = 16 over 151,936 float32 logits
     and the 2560 -> 1024 router on one float32 hidden state."""

@@ -48,3 +48,11 @@ def test_noalloc_two_calls_second_smaller():
     small = _case(32, 5, 7, 3001, 256, 64, "f32", "f32", torch.cuda.Stream())
     assert small < big
 
+
+def test_noalloc_shared_launch_then_larger():
+    # 24 bf16 chains: router tiles inside the sweep's launch; then 70 chains with a
+    # separate router launch, over more of the scratch than the first call used.
+    first = _case(33, 24, 16, 40009, 2560, 1024, "bf16", "bf16", torch.cuda.current_stream())
+    second = _case(34, 70, 16, 20011, 2560, 1024, "bf16", "bf16", torch.cuda.current_stream())
+    assert first < second
+
