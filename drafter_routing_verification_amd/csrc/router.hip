@@ -5,7 +5,7 @@
 //   - router_gemv_kernel (small batches or float32, KS = 1): one wave64 per
 //     hidden unit j streams row j of W1 once with coalesced 16-byte loads and
 //     dots it with up to 8 hidden states, reduced across the wave by DPP moves.
-//   - router_mfma_kernel (bf16 batches of 10 or more): a workgroup owns a
+//   - router_mfma_kernel (bf16 batches of 9 or more): a workgroup owns a
 //     32 (j) x 64 (b) tile and one slice of the hidden size.  All of its loads
 //     are issued up front as row-contiguous 16-byte loads, staged chunk by
 //     chunk through LDS, and multiplied with v_mfma_f32_16x16x32_bf16 (float32
@@ -41,12 +41,15 @@ constexpr int kChunksInFlight = 5;  // chunks whose loads are issued together
 constexpr int64_t kRouterWorkgroups = WF_ROUTER_WGS;
 // Smallest bf16 batch routed on MFMA tiles; smaller batches (and float32) take the GEMV.
 // Same box, whole whiflash_round_chain step over 151,936-wide rows, hidden 2560, m = 1024
-// (m = 320), median of three trials, GEMV -> MFMA: 9 sequences 21.4 -> 21.3 us (20.9 ->
-// 21.3); 10: 22.0 -> 21.1 (21.6 -> 21.2); 12: 24.0 -> 21.2 (22.9 -> 21.4); 15: 26.7 ->
-// 23.0 (25.4 -> 22.9); 16: 27.4 -> 23.6 (25.9 -> 23.3); 32: 41.7 -> 35.7; 256: 248.9 ->
-// 213.1 (216.5 -> 200.3).  Up to 8 sequences the GEMV shares the sweep's launch instead.
+// (m = 320), median of three trials, GEMV -> MFMA, each router in a launch of its own:
+// 9 sequences 21.4 -> 21.3 us (20.9 -> 21.3); 10: 22.0 -> 21.1 (21.6 -> 21.2); 12: 24.0
+// -> 21.2 (22.9 -> 21.4); 15: 26.7 -> 23.0 (25.4 -> 22.9); 16: 27.4 -> 23.6 (25.9 ->
+// 23.3); 32: 41.7 -> 35.7; 256: 248.9 -> 213.1 (216.5 -> 200.3).  With small MFMA
+// routers sharing the sweep's launch (round.hip), two trials: 9 sequences 21.2-21.4 ->
+// 17.9 us (20.8-21.1 -> 17.9); up to 8 sequences, where the GEMV tiles share the sweep's
+// launch too, the GEMV stays 0.1-0.3 us ahead (1, 2, 4 and 8 sequences measured).
 #ifndef WF_ROUTER_MFMA_MIN_BATCH
-#define WF_ROUTER_MFMA_MIN_BATCH 10
+#define WF_ROUTER_MFMA_MIN_BATCH 9
 #endif
 constexpr int32_t kMfmaMinBatch = WF_ROUTER_MFMA_MIN_BATCH;
 

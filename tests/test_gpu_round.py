@@ -167,11 +167,11 @@ def test_round_chain_batched_chain_config():
     _chain_round(r, batch, dev(batch.logits), r.b1, 0.0)
 
 
-@pytest.mark.parametrize("B", [9, 10, 12, 15, 16, 24, 32, 33])
+@pytest.mark.parametrize("B", [8, 9, 10, 12, 15, 16, 24, 32, 33])
 def test_round_chain_mid_batches(B):
-    """9 to 33 sequences on 16-byte aligned operands, around the MFMA router's 10-sequence
-    switch (the GEMV router below it; two launches per round up to 8 sequences, three from
-    9 on)."""
+    """8 to 33 sequences on 16-byte aligned operands, around the MFMA router's 9-sequence
+    switch (below it the GEMV router's tiles share the sweep's launch; from 9 on the MFMA
+    router's tiles do, up to the size where it takes a launch of its own)."""
     from synth import make_chain_batch
     print(f"round_chain batch tiles B={B}", flush=True)
     r = make_router_inputs(B + 500, B, 2560, 1024, "bf16")
