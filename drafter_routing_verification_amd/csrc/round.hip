@@ -1,14 +1,22 @@
 // One routed speculation round (WhiFlash paper, sections 3.2 and 3.3): the
 // neural router, then greedy verification of each sequence with the drafter
-// the router chose.  Also the chain-only round: the router (its choice is for
-// the next round) and the DFlash verification, sharing one final kernel.  Same results as whiflash_route followed by
-// whiflash_verify_routed, in three launches instead of four: router stage 1,
-// the argmax sweep, then one kernel per sequence that finishes the router
-// (Delta-AL and the drafter choice) and verifies the sequence with it.
-// (Running the router's MFMA workgroups inside the sweep's launch was measured
-// slower: latency-bound router tiles stretched the 217 us sweep to 245 us.  For
-// a few sequences on the GEMV router path, router stage 1 and the sweep do
-// share one launch: two launches per round instead of three.)
+// the router chose; and the chain-only round: the router (its choice is for the
+// next round) and the DFlash verification.  Same results as whiflash_route
+// followed by whiflash_verify_routed (or whiflash_verify_chain), in fewer
+// launches: router stage 1 and the argmax sweep, then one kernel per sequence
+// that finishes the router (Delta-AL and the drafter choice) and verifies the
+// sequence.
+//
+// Router stage 1 takes one of three forms:
+//   - up to 8 sequences on the GEMV path: its GEMV tiles share the sweep's
+//     launch (router_sweep_kernel), two launches per round;
+//   - a small MFMA router (at most WF_ROUTER_INTERLEAVE_LOADS chunk loads): its
+//     lean tiles share the sweep's launch, spread through the first part of every
+//     XCD's workgroups (router_mfma_sweep_kernel), two launches per round;
+//   - a larger one: a launch of its own (router.hip), three launches per round.
+//     Its tiles inside the sweep's launch, heavy or lean, spread or trailing,
+//     measured slower: under a sweep that saturates HBM they hold their slots
+//     through long chains of loads.
 #include "accept.h"
 #include "common.h"
 #include "gemv_body.h"

@@ -272,12 +272,13 @@ size_t whiflash_round_workspace_bytes(int32_t B, int32_t m, int32_t total_rows, 
  * the same arguments, results and error codes as the two calls (hidden_dtype
  * is the router's element type, logits_dtype the logits').  It runs in three
  * launches instead of four: router stage 1, the argmax sweep, then one kernel
- * per sequence that finishes the router and verifies the sequence.  With at
- * most 8 sequences, 16-byte aligned hidden and W1 and d a multiple of 16 bytes
- * of elements (the router's GEMV path), router stage 1 and the sweep share one
- * launch: two in all.  Callers
- * that cannot fuse the two steps (e.g. a different stream for each) use the
- * separate entry points.
+ * per sequence that finishes the router and verifies the sequence.  Router
+ * stage 1 and the sweep share one launch (two in all) when the hidden states
+ * and W1 are 16-byte aligned with d a multiple of 16 bytes of elements and
+ * either there are at most 8 sequences (the router's GEMV path) or the bf16
+ * router is small (at most 2,048 64-column chunk loads of its MFMA tiles, e.g.
+ * up to 64 sequences at 2560 -> 1024).  Callers that cannot fuse the two steps
+ * (e.g. a different stream for each) use the separate entry points.
  */
 int32_t whiflash_round_routed(const void* hidden, int32_t hidden_dtype, int32_t d, const void* W1,
                               const float* b1, int32_t m, const void* W2, const float* b2,
@@ -450,8 +451,8 @@ size_t whiflash_round_chain_workspace_bytes(int32_t B, int32_t m, int32_t K, int
  * next round) and whiflash_verify_chain on this round's logits and drafts, in
  * three launches instead of four (router stage 1; the argmax sweep; one
  * kernel per sequence that finishes the router and scans the chain), or two
- * when router stage 1 and the sweep share a launch (as in whiflash_round_routed:
- * at most 8 sequences on the router's GEMV path).
+ * when router stage 1 and the sweep share a launch (under the same conditions
+ * as in whiflash_round_routed).
  * Arguments, layouts and errors are those of the two calls; delta_al, choice,
  * accept_len, bonus and row_argmax equal theirs.  Workspace:
  * whiflash_round_chain_workspace_bytes(B, m, K, V) bytes, 256-byte aligned.
