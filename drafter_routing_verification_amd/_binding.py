@@ -629,8 +629,8 @@ def round_routed(hidden, W1, b1, W2, b2, tau: float, logits, row_offsets, total_
                  chain_draft, parent, draft_ids, d2t, *, row_argmax=True, delta_al=None,
                  choice=None, accept_len=None, bonus=None, best_node=None, workspace=None,
                  stream=None, _early=False):
-    """route + verify_routed in one call (three launches; two for up to 8 sequences on the
-    GEMV router path).  Returns (delta_al, choice, accept_len, bonus, best_node,
+    """route + verify_routed in one call (three launches; two when the router is small enough
+    to share the sweep's launch).  Returns (delta_al, choice, accept_len, bonus, best_node,
     row_argmax)."""
     _device_tensor(hidden, "hidden")
     B, d = hidden.shape
@@ -733,9 +733,9 @@ def verify_routed_entropy(logits, row_offsets, total_rows: int, choice, chain_dr
 def round_chain(hidden, W1, b1, W2, b2, tau: float, logits, draft, *, row_argmax=True,
                 delta_al=None, choice=None, accept_len=None, bonus=None, workspace=None,
                 stream=None, _early=False):
-    """route + verify_chain in one call (three launches; two for up to 8 sequences on the
-    GEMV router path).  hidden [B, d]; logits [B*(K+1), V] or [B, K+1, V]; draft [B, K]
-    int32.  Returns (delta_al, choice, accept_len, bonus, row_argmax)."""
+    """route + verify_chain in one call (three launches; two when the router is small enough
+    to share the sweep's launch).  hidden [B, d]; logits [B*(K+1), V] or [B, K+1, V]; draft
+    [B, K] int32.  Returns (delta_al, choice, accept_len, bonus, row_argmax)."""
     _device_tensor(hidden, "hidden")
     B, d = hidden.shape
     m = W1.shape[0]
