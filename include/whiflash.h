@@ -499,8 +499,8 @@ int32_t whiflash_round_chain_early_exit(const void* hidden, int32_t hidden_dtype
  * copy per GPU, held until the process ends.  The call allocates nothing.
  *   - A round whose whiflash_round_chain_workspace_bytes(B, m, K, V) exceeds
  *     WHIFLASH_NOALLOC_SCRATCH_BYTES returns WF_ERR_SCRATCH and launches
- *     nothing (about 1,400 sequences at K = 16, V = 151,936, m = 1024; 256
- *     sequences need 2.4 MB).
+ *     nothing (past 1,367 sequences at K = 16, V = 151,936, m = 1024; 256
+ *     sequences need 2.6 MB).
  *   - The GPU is the stream's device (the current device for stream 0).  The
  *     first call on each GPU looks up that GPU's address of the array
  *     (WF_ERR_RUNTIME if the runtime cannot give it); later calls reuse it.
