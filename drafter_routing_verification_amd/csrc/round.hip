@@ -105,9 +105,11 @@ __global__ __launch_bounds__(kThreads) void round_chain_finalize_kernel(
   chain_accept(draft0, t_s, K, dr, accept_len + b, bonus + b, nullptr);
 }
 
-// First launch of a small-batch round: workgroups [0, router_blocks) run the
-// router's GEMV tiles (workgroup i: hidden units 4 i .. 4 i + 3 for every
-// sequence, all B <= NB of them), the rest run the argmax sweep's chunks.
+// First launch of a small-batch round: router_blocks workgroups run the
+// router's GEMV tiles (router workgroup i: hidden units 4 i .. 4 i + 3 for every
+// sequence, all B <= NB of them), the rest run the argmax sweep's chunks.  The
+// router's workgroups come first, or last when router_last is set (the sweep's
+// chunks are then dispatched first).
 // The two halves read disjoint inputs and write disjoint outputs.  At a few
 // sequences both are small and latency-bound, so one launch instead of two
 // saves a launch floor; at large batches the router runs on MFMA tiles in a
@@ -115,16 +117,18 @@ __global__ __launch_bounds__(kThreads) void round_chain_finalize_kernel(
 template <int DTL, int DTH, int NB>
 __global__ __launch_bounds__(kThreads) void router_sweep_kernel(
     const void* __restrict__ hidden, int B, int d, const void* __restrict__ W1, int m,
-    float* __restrict__ zp, int router_blocks, const unsigned char* __restrict__ logits,
-    int64_t row_bytes, int V, int splits, int chunk_vecs, int nvec, Partial* __restrict__ part) {
-  const int i = blockIdx.x;
-  if (i < router_blocks) {
+    float* __restrict__ zp, int router_blocks, int router_last,
+    const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
+    int chunk_vecs, int nvec, Partial* __restrict__ part) {
+  const int nsweep = static_cast<int>(gridDim.x) - router_blocks;
+  const int i = static_cast<int>(blockIdx.x) - (router_last ? nsweep : 0);  // router workgroup
+  if (i >= 0 && i < router_blocks) {
     const HiddenSel direct{nullptr, nullptr, 0, 0};
     gemv_tile<DTH, NB, true>(i, 0, hidden, direct, B, d, W1, m, zp);
   } else {
     // Few rows, few workgroups per CU: each thread issues its whole batch of loads at once.
-    sweep_chunk<DTL, kThreads, true>(i - router_blocks, logits, row_bytes, V, splits, chunk_vecs,
-                                     nvec, part);
+    const int c = router_last ? static_cast<int>(blockIdx.x) : i - router_blocks;
+    sweep_chunk<DTL, kThreads, true>(c, logits, row_bytes, V, splits, chunk_vecs, nvec, part);
   }
 }
 
@@ -152,13 +156,14 @@ __global__ __launch_bounds__(kThreads) void router_mfma_sweep_kernel(
 template <int DTL, int DTH>
 hipError_t launch_router_sweep_nb(unsigned grid, int nb, const void* hidden, int B, int d,
                                   const void* W1, int m, float* zp, int router_blocks,
-                                  const unsigned char* logits, int64_t row_bytes, int V,
+                                  int router_last, const unsigned char* logits, int64_t row_bytes,
+                                  int V,
                                   int splits, int chunk_vecs, int nvec, Partial* part,
                                   hipStream_t stream) {
 #define WF_ROUTER_SWEEP(NBV)                                                                   \
   hipLaunchKernelGGL((router_sweep_kernel<DTL, DTH, NBV>), dim3(grid), dim3(kThreads), 0, stream, \
-                     hidden, B, d, W1, m, zp, router_blocks, logits, row_bytes, V, splits,      \
-                     chunk_vecs, nvec, part)
+                     hidden, B, d, W1, m, zp, router_blocks, router_last, logits, row_bytes, V, \
+                     splits, chunk_vecs, nvec, part)
   if (nb == 1) WF_ROUTER_SWEEP(1);
   else if (nb == 2) WF_ROUTER_SWEEP(2);
   else if (nb == 4) WF_ROUTER_SWEEP(4);
@@ -256,27 +261,22 @@ hipError_t launch_round_stage1(bool fused, const RouterPlan& plan, int hidden_dt
     return launch_sweep(logits, logits_dtype, row_stride, rows, V, sp, part, stream);
   }
   const int nb = B == 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;
+  // One sequence: its sweep chunks are dispatched ahead of the router's tiles.
+  const int last = B == 1 ? 1 : 0;
   const unsigned grid = static_cast<unsigned>(router_gx + sweep_blocks);
   const unsigned char* base = static_cast<const unsigned char*>(logits);
   const int gx = static_cast<int>(router_gx);
-  if (logits_dtype == WF_BF16) {
-    using E = Elem<WF_BF16>;
-    const int64_t rb = row_stride * E::kBytes;
-    const int cv = sp.chunk / E::kPerVec, nv = V / E::kPerVec;
-    return hidden_dtype == WF_BF16
-               ? launch_router_sweep_nb<WF_BF16, WF_BF16>(grid, nb, hidden, B, d, W1, m, zp, gx,
-                                                          base, rb, V, sp.splits, cv, nv, part, stream)
-               : launch_router_sweep_nb<WF_BF16, WF_F32>(grid, nb, hidden, B, d, W1, m, zp, gx,
-                                                         base, rb, V, sp.splits, cv, nv, part, stream);
-  }
-  using E = Elem<WF_F32>;
-  const int64_t rb = row_stride * E::kBytes;
-  const int cv = sp.chunk / E::kPerVec, nv = V / E::kPerVec;
-  return hidden_dtype == WF_BF16
-             ? launch_router_sweep_nb<WF_F32, WF_BF16>(grid, nb, hidden, B, d, W1, m, zp, gx,
-                                                       base, rb, V, sp.splits, cv, nv, part, stream)
-             : launch_router_sweep_nb<WF_F32, WF_F32>(grid, nb, hidden, B, d, W1, m, zp, gx,
-                                                      base, rb, V, sp.splits, cv, nv, part, stream);
+  const bool bf16_logits = logits_dtype == WF_BF16;
+  const int per = bf16_logits ? Elem<WF_BF16>::kPerVec : Elem<WF_F32>::kPerVec;
+  const int64_t rb = row_stride * (bf16_logits ? Elem<WF_BF16>::kBytes : Elem<WF_F32>::kBytes);
+  const int cv = sp.chunk / per, nv = V / per;
+#define WF_STAGE1(DTL, DTH)                                                                      \
+  launch_router_sweep_nb<DTL, DTH>(grid, nb, hidden, B, d, W1, m, zp, gx, last, base, rb, V,   \
+                                   sp.splits, cv, nv, part, stream)
+  if (bf16_logits)
+    return hidden_dtype == WF_BF16 ? WF_STAGE1(WF_BF16, WF_BF16) : WF_STAGE1(WF_BF16, WF_F32);
+  return hidden_dtype == WF_BF16 ? WF_STAGE1(WF_F32, WF_BF16) : WF_STAGE1(WF_F32, WF_F32);
+#undef WF_STAGE1
 }
 
 hipError_t launch_round_finalize(int hidden_dtype, const RouterPlan& plan, const float* zp, int32_t B,
