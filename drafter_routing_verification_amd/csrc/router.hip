@@ -6,10 +6,10 @@
 //     hidden unit j streams row j of W1 once with coalesced 16-byte loads and
 //     dots it with up to 8 hidden states, reduced across the wave by DPP moves.
 //   - router_mfma_kernel (bf16 batches of 9 or more): a workgroup owns a
-//     32 (j) x 64 (b) tile and one slice of the hidden size.  All of its loads
-//     are issued up front as row-contiguous 16-byte loads, staged chunk by
-//     chunk through LDS, and multiplied with v_mfma_f32_16x16x32_bf16 (float32
-//     accumulate).  Splitting the hidden size across workgroups keeps every CU
+//     32 (j) x 64 (b) tile and one slice of the hidden size.  Its operands
+//     arrive as row-contiguous 16-byte loads, a few chunks ahead, are staged
+//     chunk by chunk through two LDS buffers, and are multiplied with
+//     v_mfma_f32_16x16x32_bf16 (float32 accumulate).  Splitting the hidden size across workgroups keeps every CU
 //     busy: at 256 sequences of 2560 -> 1024, two slices give 256 workgroups
 //     of 96 rows x 1280 columns (240 KiB of operands each, not 480 KiB).
 // Stage 2, router_finish_kernel, one workgroup per sequence: sums the KS
@@ -30,7 +30,18 @@ constexpr int kChunk = 128;         // hidden-size columns staged through LDS at
 constexpr int kStageRows = kMfmaTileJ + kMfmaTileB;
 constexpr int kStageStride = kChunk + 8;                      // padded row (elements)
 constexpr int kPiecesPerThread = kStageRows * (kChunk / 8) / kThreads;  // 16-byte pieces
-constexpr int kChunksInFlight = 5;  // chunks whose loads are issued together
+// Chunks whose loads are in flight at once: the next kRing - 1 chunks load while
+// one is staged and multiplied.  Kernel trace of router stage 1 on 256 sequences
+// of 2560 -> 1024 (median, one box): the earlier form (batches of 5 chunks loaded
+// together through flat pointers, then staged one by one, two barriers per
+// chunk) 10.68 us; this form with two LDS buffers and one barrier per chunk, 3 /
+// 4 / 5 chunks in flight: 8.68 / 8.88 / 9.08 us; one LDS buffer, 3 / 4 in
+// flight: 9.24 / 9.36 us.  Another box: 10.28 -> 9.44 us (m = 1024), 7.36 ->
+// 6.56 us (m = 320).  The bench steps moved less than their spread.
+#ifndef WF_ROUTER_RING
+#define WF_ROUTER_RING 3
+#endif
+constexpr int kRing = WF_ROUTER_RING;
 #ifndef WF_ROUTER_WGS
 #define WF_ROUTER_WGS 256
 #endif
@@ -66,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
 }
 
 // One workgroup = 4 waves per 32 (j) x 64 (b) tile of z^T and one slice
-// [k0, k1) of the hidden size.  Rows 0..31 of the staging area hold W1 rows
+// [k0, k1) of the hidden size.  Rows 0..31 of a staging buffer hold W1 rows
 // j0.., rows 32..95 hold hidden rows bb0..; each row chunk is kChunk wide.
 // Wave w computes the 16 x 16 accumulators (j-subtile w & 1) x (b-subtiles
 // 2 (w >> 1) and 2 (w >> 1) + 1).
@@ -74,12 +85,26 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(
 // the A tile and column (l % 16) of the B tile, 8 consecutive k values starting
 // at 8 * (l / 16); the accumulator of lane l holds rows 4 * (l / 16) + i,
 // i = 0..3, of column l % 16.
+//
+// Operands stream through a ring of kRing chunks held in registers: chunk c is
+// staged into LDS buffer c & 1 while chunks c + 1 .. c + kRing - 1 are still
+// loading, and its slot is refilled with chunk c + kRing right after the
+// barrier.  Two buffers need one barrier per chunk: a wave writes buffer c & 1
+// only after the barrier of chunk c - 1, which every wave reaches after its
+// multiplies of chunk c - 2.  The loads go through global (not flat) pointers,
+// so waiting on LDS traffic never waits on them.
+// NCH > 0: no slice has more than NCH chunks, and the chunk loop is unrolled
+// whole, so each wait names exactly the loads it needs (in a loop the compiler
+// waits for every load at the top of each pass).  NCH == 0: the count is read
+// at run time.
+template <int NCH>
 __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
     const unsigned short* __restrict__ hidden, HiddenSel sel, int B, int d,
     const unsigned short* __restrict__ W1, int m, int kslice, float* __restrict__ zp,
     ZeroFill zero) {
+  typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
   zero_fill_first_block(zero);
-  __shared__ __attribute__((aligned(16))) unsigned short stage[kStageRows * kStageStride];
+  __shared__ __attribute__((aligned(16))) unsigned short stage[2][kStageRows * kStageStride];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j0 = blockIdx.x * kMfmaTileJ, bb0 = blockIdx.y * kMfmaTileB, slice = blockIdx.z;
   const int k0 = slice * kslice, k1 = min(d, k0 + kslice);
@@ -88,56 +113,75 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
   // Rows this thread stages: row = i * 16 + (tid >> 4), piece column tid & 15.
   const int prow = tid >> 4, pcol = (tid & 15) * 8;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  // Source row of each piece this thread stages (nullptr: zeros).
+  // Source row of each piece this thread stages.  Rows past m or B (or without
+  // a hidden row) read row 0 of W1, always valid, and are staged as zeros.
   const unsigned short* src[kPiecesPerThread];
+  bool live[kPiecesPerThread];
 #pragma unroll
   for (int i = 0; i < kPiecesPerThread; ++i) {
     const int row = i * 16 + prow;
-    src[i] = nullptr;
     if (row < kMfmaTileJ) {
-      if (j0 + row < m) src[i] = W1 + static_cast<int64_t>(j0 + row) * d;
-    } else if (bb0 + row - kMfmaTileJ < B) {
-      const int64_t h = hidden_row(sel, bb0 + row - kMfmaTileJ);
-      if (h >= 0) src[i] = hidden + h * d;
+      live[i] = j0 + row < m;
+      src[i] = live[i] ? W1 + static_cast<int64_t>(j0 + row) * d : W1;
+    } else {
+      const int b = bb0 + row - kMfmaTileJ;
+      const int64_t h = b < B ? hidden_row(sel, b) : -1;
+      live[i] = h >= 0;
+      src[i] = live[i] ? hidden + h * d : W1;
     }
   }
-  const int nchunks = (k1 - k0 + kChunk - 1) / kChunk;
-  for (int c0 = 0; c0 < nchunks; c0 += kChunksInFlight) {
-    u32x4 buf[kChunksInFlight][kPiecesPerThread];
+  const int nreal = (k1 - k0 + kChunk - 1) / kChunk;  // this slice's chunks
+  const int nchunks = NCH > 0 ? NCH : nreal;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  auto in_range = [&](int c, int i) { return live[i] && c < nreal && k0 + c * kChunk + pcol < k1; };
+  // Loads are unconditional (a clamped address where the piece is out of
+  // range); the range is applied when the chunk is staged, so nothing waits
+  // on a load before its data is staged.
+  auto load = [&](int c, u32x4 (&slot)[kPiecesPerThread]) {
 #pragma unroll
-    for (int c = 0; c < kChunksInFlight; ++c) {
-#pragma unroll
-      for (int i = 0; i < kPiecesPerThread; ++i) {
-        const int k = k0 + (c0 + c) * kChunk + pcol;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (src[i] != nullptr && c0 + c < nchunks && k < k1)
-          v = *reinterpret_cast<const u32x4*>(src[i] + k);
-        buf[c][i] = v;
-      }
+    for (int i = 0; i < kPiecesPerThread; ++i) {
+      const int k = in_range(c, i) ? k0 + c * kChunk + pcol : 0;
+      slot[i] = *reinterpret_cast<global_u32x4*>(reinterpret_cast<uintptr_t>(src[i] + k));
     }
+  };
+  auto chunk = [&](int c, u32x4 (&slot)[kPiecesPerThread]) {
+    unsigned short* st = stage[c & 1];
 #pragma unroll
-    for (int c = 0; c < kChunksInFlight; ++c) {
-      if (c0 + c >= nchunks) break;
-      __syncthreads();
+    for (int i = 0; i < kPiecesPerThread; ++i)
+      *reinterpret_cast<u32x4*>(&st[(i * 16 + prow) * kStageStride + pcol]) =
+          in_range(c, i) ? slot[i] : zero4;
+    __syncthreads();
+    if (c + kRing < nchunks) load(c + kRing, slot);
+    if (c >= nreal) return;  // a shorter last slice: nothing to multiply
 #pragma unroll
-      for (int i = 0; i < kPiecesPerThread; ++i)
-        *reinterpret_cast<u32x4*>(&stage[(i * 16 + prow) * kStageStride + pcol]) = buf[c][i];
-      __syncthreads();
-#pragma unroll
-      for (int st = 0; st < kChunk / 32; ++st) {
-        const int col = st * 32 + g * 8;
-        const bf16x8 fa = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&stage[(a * 16 + r) * kStageStride + col]));
-        const bf16x8 f0 = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(
-                        &stage[(kMfmaTileJ + bq * 16 + r) * kStageStride + col]));
-        const bf16x8 f1 = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(
-                        &stage[(kMfmaTileJ + (bq + 1) * 16 + r) * kStageStride + col]));
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f1, acc1, 0, 0, 0);
-      }
+    for (int stp = 0; stp < kChunk / 32; ++stp) {
+      const int col = stp * 32 + g * 8;
+      const bf16x8 fa = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(&st[(a * 16 + r) * kStageStride + col]));
+      const bf16x8 f0 = __builtin_bit_cast(
+          bf16x8,
+          *reinterpret_cast<const u32x4*>(&st[(kMfmaTileJ + bq * 16 + r) * kStageStride + col]));
+      const bf16x8 f1 = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(
+                      &st[(kMfmaTileJ + (bq + 1) * 16 + r) * kStageStride + col]));
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f1, acc1, 0, 0, 0);
     }
+  };
+  u32x4 ring[kRing][kPiecesPerThread];
+#pragma unroll
+  for (int q = 0; q < kRing; ++q) load(q, ring[q]);
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int c0 = 0; c0 < NCH; c0 += kRing)
+#pragma unroll
+      for (int q = 0; q < kRing; ++q)
+        if (c0 + q < NCH) chunk(c0 + q, ring[q]);
+  } else {
+    for (int c0 = 0; c0 < nchunks; c0 += kRing)
+#pragma unroll
+      for (int q = 0; q < kRing; ++q)
+        if (c0 + q < nchunks) chunk(c0 + q, ring[q]);
   }
   // z partials: lane holds j = j0 + 16a + 4g + i for one b per accumulator.
   const int jb = j0 + a * 16 + g * 4;
@@ -220,9 +264,27 @@ hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, cons
   if (plan.mfma) {
     const dim3 grid((m + kMfmaTileJ - 1) / kMfmaTileJ, (B + kMfmaTileB - 1) / kMfmaTileB,
                     plan.slices);
-    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(kThreads), 0, stream,
-                       static_cast<const unsigned short*>(hidden), sel, B, d,
-                       static_cast<const unsigned short*>(W1), m, plan.kslice, zp, zero);
+    const unsigned short* h = static_cast<const unsigned short*>(hidden);
+    const unsigned short* w1 = static_cast<const unsigned short*>(W1);
+#define WF_MFMA(N)                                                                              \
+  hipLaunchKernelGGL(router_mfma_kernel<N>, grid, dim3(kThreads), 0, stream, h, sel, B, d, w1, m, \
+                     plan.kslice, zp, zero)
+    // The chunk counts of the usual slicings (2,560 or 4,096 wide hidden states
+    // at 9 to 65,535 sequences); any other count takes the run-time loop.
+    switch (plan.kslice / kChunk) {
+      case 3: WF_MFMA(3); break;
+      case 4: WF_MFMA(4); break;
+      case 5: WF_MFMA(5); break;
+      case 6: WF_MFMA(6); break;
+      case 7: WF_MFMA(7); break;
+      case 8: WF_MFMA(8); break;
+      case 10: WF_MFMA(10); break;
+      case 16: WF_MFMA(16); break;
+      case 20: WF_MFMA(20); break;
+      case 32: WF_MFMA(32); break;
+      default: WF_MFMA(0); break;
+    }
+#undef WF_MFMA
     return hipGetLastError();
   }
   const int per = dtype == WF_BF16 ? 8 : 4;
