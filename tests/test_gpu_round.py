@@ -1,6 +1,9 @@
-"""GPU parity of the fused round (whiflash_round_routed = route + verify_routed in three
-launches) against the oracle's route followed by its routed verification, and
-agreement with the two separate GPU calls (the router may be summed in another order)."""
+"""GPU parity of the fused rounds (whiflash_round_routed = route + verify_routed, and
+whiflash_round_chain = route + verify_chain, in fewer launches) against the oracle's route
+followed by its verification, and bit-for-bit agreement with the separate GPU calls: router
+stage 1 runs the same arithmetic in both (the GEMV tile, the MFMA tile or its lean form
+inside the sweep's launch, over the same slices in the same step order), and the finish is
+shared code."""
 
 import functools
 
@@ -24,14 +27,9 @@ def _run(r, rb, logits, b2):
     sep = [host(x) for x in wf.verify_routed(logits, dev(rb.offsets), rb.rows, ch,
                                              dev(rb.chain_draft), dev(rb.parent),
                                              dev(rb.draft_ids), dev(rb.d2t))]
-    # The fused round may sum the router in another order than whiflash_route:
-    # the two float32 results agree closely, and so does everything downstream.
     dal_s, ch_s = host(dal), host(ch)
-    assert np.all(np.abs(out[0] - dal_s) <= 1e-4 * np.maximum(1.0, np.abs(dal_s)))
-    same = out[1] == ch_s
-    assert np.all(same | (np.abs(dal_s - r.tau) < 1e-3))
-    assert all(np.array_equal(a[same], b[same]) for a, b in zip(out[2:5], sep[:3]))
-    assert np.array_equal(out[5], sep[3])
+    assert np.array_equal(out[0], dal_s) and np.array_equal(out[1], ch_s)
+    assert all(np.array_equal(a, b) for a, b in zip(out[2:6], sep))
     return out
 
 
@@ -97,8 +95,7 @@ def _chain_round(r, cb, logits, b1, b2):
     out = [host(x) for x in wf.round_chain(h, W1, b1d, W2, b2, r.tau, logits, dev(cb.draft))]
     dal, ch = (host(x) for x in wf.route(h, W1, b1d, W2, b2, r.tau))
     al, bo, rows = (host(x) for x in wf.verify_chain(logits, dev(cb.draft)))
-    assert np.all(np.abs(out[0] - dal) <= 1e-4 * np.maximum(1.0, np.abs(dal)))
-    assert np.all((out[1] == ch) | (np.abs(dal - r.tau) < 1e-3))
+    assert np.array_equal(out[0], dal) and np.array_equal(out[1], ch)
     assert np.array_equal(out[2], al) and np.array_equal(out[3], bo)
     assert np.array_equal(out[4], rows)
     e_dal, e_ch = oracle.route(r.hidden, r.W1, b1, r.W2, np.float32(b2), r.tau, r.dtype)
