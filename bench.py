@@ -18,6 +18,13 @@ Workloads:
   llama: the throughput sweep at Llama-3.1-8B shapes: 256 chains, K = 10, bf16
       logits [256, 11, 128256] (722 MB per round), router 4096 -> 512 -> 1;
       100 resident rounds.
+  single: one DFlash chain, K = 16, float32 logits [17, 151936] and the router
+      on one float32 hidden state; a launch-latency-bound size, so every figure
+      comes from replaying a captured HIP graph of 16 resident rounds.
+  chain32: 32 DFlash chains, K = 16, bf16 logits [32, 17, 151936] with the
+      router (its tiles share the sweep's launch).
+  trees: 8 EAGLE-3 trees of 61 nodes over bf16 logits, no router; one step is
+      whiflash_verify_tree.
 
 Prints one JSON line (rounds/s, logits GB/s, roofline of the argmax sweep and
 the CPU oracle baseline).
