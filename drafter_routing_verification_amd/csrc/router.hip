@@ -9,9 +9,10 @@
 //     32 (j) x 64 (b) tile and one slice of the hidden size.  Its operands
 //     arrive as row-contiguous 16-byte loads, a few chunks ahead, are staged
 //     chunk by chunk through two LDS buffers, and are multiplied with
-//     v_mfma_f32_16x16x32_bf16 (float32 accumulate).  Splitting the hidden size across workgroups keeps every CU
-//     busy: at 256 sequences of 2560 -> 1024, two slices give 256 workgroups
-//     of 96 rows x 1280 columns (240 KiB of operands each, not 480 KiB).
+//     v_mfma_f32_16x16x32_bf16 (float32 accumulate).  Splitting the hidden
+//     size across workgroups keeps every CU busy: at 256 sequences of
+//     2560 -> 1024, two slices give 256 workgroups of 96 rows x 1280 columns
+//     (240 KiB of operands each, not 480 KiB).
 // Stage 2, router_finish_kernel, one workgroup per sequence: sums the KS
 // partials, adds b1, applies GELU and W2, sums over j and adds b2, all in
 // float32 and in a fixed order (bitwise reproducible), then thresholds.
@@ -46,9 +47,11 @@ constexpr int kRing = WF_ROUTER_RING;
 #define WF_ROUTER_WGS 256
 #endif
 // MFMA grid size the slicing of the hidden size aims for.  On 256 sequences of
-// 2560 -> 1024 (bench step, same process, two interleaved trials): 256
-// workgroups (2 slices) route 15.8 us; 512 (4 slices, two per CU, each with one
-// load batch) 15.6 us and the same step time; 1024 (7 slices) 19.0 us.
+// 2560 -> 1024 (bench step, same process, two interleaved trials, the kernel
+// before its ring of chunks): 256 workgroups (2 slices) route 15.8 us; 512 (4
+// slices, two per CU, each with one load batch) 15.6 us and the same step
+// time; 1024 (7 slices) 19.0 us.  With the ring, kernel trace: 256 workgroups
+// 9.12-9.36 us, 512 9.28-9.72 us, 1024 12.08 us.
 constexpr int64_t kRouterWorkgroups = WF_ROUTER_WGS;
 // Smallest bf16 batch routed on MFMA tiles; smaller batches (and float32) take the GEMV.
 // Same box, whole whiflash_round_chain step over 151,936-wide rows, hidden 2560, m = 1024
