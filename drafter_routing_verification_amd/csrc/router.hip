@@ -29,7 +29,11 @@ constexpr int kMfmaTileJ = 32;      // hidden units per MFMA workgroup tile
 constexpr int kMfmaTileB = 64;      // sequences per MFMA workgroup tile
 constexpr int kChunk = 128;         // hidden-size columns staged through LDS at a time
 constexpr int kStageRows = kMfmaTileJ + kMfmaTileB;
-constexpr int kStageStride = kChunk + 8;                      // padded row (elements)
+// Rows padded by 16 elements (288 bytes apart): no LDS bank conflicts in the
+// staging writes or the fragment reads.  Padded by 8, 24 or 32 elements, the
+// SQ_LDS_BANK_CONFLICT counter read a third of the LDS's active cycles (256
+// sequences of 2560 -> 1024: 368,640 of 1,105,920; padded by 16: 0 of 737,280).
+constexpr int kStageStride = kChunk + 16;
 constexpr int kPiecesPerThread = kStageRows * (kChunk / 8) / kThreads;  // 16-byte pieces
 // Chunks whose loads are in flight at once: the next kRing - 1 chunks load while
 // one is staged and multiplied.  Kernel trace of router stage 1 on 256 sequences

@@ -3,7 +3,7 @@
 // 32 (hidden units) x 64 (sequences) tile and the same sequence of
 // v_mfma_f32_16x16x32_bf16 steps over one slice of the hidden size as
 // router_mfma_kernel, so its partial sums are bitwise the same.  It differs in
-// how operands reach the matrix cores: 64 columns at a time through 13.5 KiB of
+// how operands reach the matrix cores: 64 columns at a time through 15 KiB of
 // LDS, with the next 64 columns' loads in flight while the current ones are
 // multiplied, so it needs few registers and little LDS and does not lower the
 // occupancy of the sweep's workgroups in the same launch.
@@ -18,7 +18,7 @@ constexpr int kTileJ = 32;                                 // hidden units per t
 constexpr int kTileB = 64;                                 // sequences per tile
 constexpr int kLeanChunk = 64;                             // columns staged per step
 constexpr int kLeanRows = kTileJ + kTileB;                 // W1 rows, then hidden rows
-constexpr int kLeanStride = kLeanChunk + 8;                // padded LDS row (elements)
+constexpr int kLeanStride = kLeanChunk + 16;  // padded LDS row (elements): no bank conflicts
 constexpr int kLeanPieces = kLeanRows * (kLeanChunk / 8) / kThreads;  // 16-byte pieces per thread
 static_assert(kLeanPieces * kThreads == kLeanRows * (kLeanChunk / 8), "pieces must tile the chunk");
 
