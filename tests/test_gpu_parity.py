@@ -181,6 +181,21 @@ def test_router_small(dtype, B, d, m):
     check_router(host(dal), host(ch), e_dal, e_ch, dtype, 0.1)
 
 
+# bf16 routers on MFMA tiles whose slicing of the hidden size gives chunk counts per slice
+# of 16, 32, 6 and 7 (the last two with a shorter last slice: 2 of 6 and 6 of 7 chunks),
+# and 9 (a count the kernel reads at run time).
+@pytest.mark.parametrize("B,d,m", [(512, 4096, 512), (512, 4096, 1024), (128, 4096, 640),
+                                   (150, 2560, 704), (300, 1152, 1024)])
+def test_router_mfma_slicings(B, d, m):
+    print(f"router MFMA slicing B={B} d={d} m={m}", flush=True)
+    r = make_router_inputs(B * 7 + d + m, B, d, m, "bf16")
+    b1 = (np.random.default_rng(m).standard_normal(m) * 0.5).astype(np.float32)
+    dal, ch = wf.route(dev(r.hidden), dev(r.W1), dev(b1), dev(r.W2), 0.125, 0.1)
+    torch.cuda.synchronize()
+    e_dal, e_ch = oracle.route(r.hidden, r.W1, b1, r.W2, np.float32(0.125), 0.1, "bf16")
+    check_router(host(dal), host(ch), e_dal, e_ch, "bf16", 0.1)
+
+
 def test_router_deterministic():
     r = make_router_inputs(5, 64, 2560, 1024, "bf16")
     args = (dev(r.hidden), dev(r.W1), None, dev(r.W2), 0.0, 1.0)
