@@ -190,7 +190,11 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
       for (int q = 0; q < kRing; ++q)
         if (c0 + q < nchunks) chunk(c0 + q, ring[q]);
   }
-  // z partials: lane holds j = j0 + 16a + 4g + i for one b per accumulator.
+  // z partials: lane holds j = j0 + 16a + 4g + i for one b per accumulator, so one
+  // 16-byte store per accumulator when m is a multiple of 4 (the rows of zp are then
+  // 16-byte aligned).  Kernel trace, 256 sequences of 2560 -> 1024: 8.64-8.72 us
+  // with four 4-byte stores, 8.00-8.08 us with one 16-byte store (7.36 us with no
+  // store at all).
   const int jb = j0 + a * 16 + g * 4;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -198,6 +202,10 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
     if (b >= B) continue;
     const f32x4 v = q == 0 ? acc0 : acc1;
     float* dst = zp + (static_cast<int64_t>(slice) * B + b) * m + jb;
+    if ((m & 3) == 0 && jb + 3 < m) {
+      *reinterpret_cast<f32x4*>(dst) = v;
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (jb + i < m) dst[i] = v[i];

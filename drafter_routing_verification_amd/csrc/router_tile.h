@@ -114,6 +114,10 @@ __device__ inline void router_lean_tile(int t, int tiles_j, int tiles_b, int KS,
     if (b >= B) continue;
     const lean_f32x4 v = q == 0 ? acc0 : acc1;
     float* dst = zp + (static_cast<int64_t>(slice) * B + b) * m + jb;
+    if ((m & 3) == 0 && jb + 3 < m) {  // 16-byte aligned: one store
+      *reinterpret_cast<lean_f32x4*>(dst) = v;
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (jb + i < m) dst[i] = v[i];
