@@ -147,9 +147,12 @@ __global__ __launch_bounds__(kThreads) void router_mfma_sweep_kernel(
   if (t < 0) {
     router_lean_tile(static_cast<int>(-t - 1), tiles_j, tiles_b, KS, hidden, B, d, W1, m, kslice,
                      zp, stage);
+  } else if (kBatch || sweep_edge_block()) {
+    sweep_chunk<DTL, kThreads, true>(static_cast<int>(t), logits, row_bytes, V, splits,
+                                     chunk_vecs, nvec, part);
   } else {
-    sweep_chunk<DTL, kThreads, kBatch>(static_cast<int>(t), logits, row_bytes, V, splits,
-                                       chunk_vecs, nvec, part);
+    sweep_chunk<DTL, kThreads, false>(static_cast<int>(t), logits, row_bytes, V, splits,
+                                      chunk_vecs, nvec, part);
   }
 }
 

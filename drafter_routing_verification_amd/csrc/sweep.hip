@@ -15,14 +15,13 @@ namespace wf {
 namespace {
 
 constexpr int kSweepThreads = WF_SWEEP_THREADS;
-constexpr unsigned kXcds = 8;  // accelerator complex dies of an MI355X
 
 // Workgroups are handed to the 8 XCDs round robin (workgroup i to XCD i % 8).
 // Renumber them so that XCD x sweeps one contiguous range of chunks, in order:
 // the n chunks are cut into 8 ranges of n / 8 (the first n % 8 one longer).
 __device__ inline int xcd_contiguous_block() {
-  const unsigned n = gridDim.x, q = n / kXcds, r = n % kXcds;
-  const unsigned x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+  const unsigned n = gridDim.x, q = n / kSweepXcds, r = n % kSweepXcds;
+  const unsigned x = blockIdx.x % kSweepXcds, k = blockIdx.x / kSweepXcds;
   return static_cast<int>(x * q + (x < r ? x : r) + k);
 }
 
@@ -46,8 +45,12 @@ template <int DT, bool kBatch>
 __global__ __launch_bounds__(kSweepThreads) void argmax_sweep_kernel(
     const unsigned char* __restrict__ logits, int64_t row_bytes, int V, int splits,
     int chunk_vecs, int nvec, Partial* __restrict__ part) {
-  sweep_chunk<DT, kSweepThreads, kBatch>(xcd_contiguous_block(), logits, row_bytes, V, splits,
+  if (kBatch || sweep_edge_block())
+    sweep_chunk<DT, kSweepThreads, true>(xcd_contiguous_block(), logits, row_bytes, V, splits,
                                          chunk_vecs, nvec, part);
+  else
+    sweep_chunk<DT, kSweepThreads, false>(xcd_contiguous_block(), logits, row_bytes, V, splits,
+                                          chunk_vecs, nvec, part);
 }
 
 // The sweep's reads without its comparisons: the same chunks, workgroups,
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(kSweepThreads) void stream_read_kernel(
   const int v1 = min(v0 + chunk_vecs, nvec);
   unsigned acc = 0;
   int v = v0 + threadIdx.x;
-  if constexpr (kBatch) {
+  if (kBatch || sweep_edge_block()) {
     for (; v < v1; v += kUnroll * kSweepThreads) {
       u32x4 d[kUnroll];
 #pragma unroll

@@ -23,6 +23,24 @@ namespace wf {
 
 constexpr int kUnroll = 8;  // 16-byte loads in flight per thread
 
+// In a large launch (every resident slot streaming, one load at a time per
+// thread), the workgroups dispatched first and the last ones of every XCD issue
+// their whole batch of loads at once instead: the first kSweepHeadBatch of the
+// grid, while the slots fill, and the last kSweepTailBatch that each XCD takes
+// (workgroup i goes to XCD i % 8), while they drain.  Each then has five times
+// the bytes in flight when few workgroups are.  Same box, two trials, back-to-back
+// sweeps alone, 4,352 / 4,992 rows of 151,936 and 2,816 rows of 128,256 bf16:
+// 181.1-181.3 / 217.2-217.9 / 101.8-102.0 us streaming everywhere; 179.0-179.2 /
+// 215.2-215.7 / 99.9-100.0 us with 4,096 head and 512 tail workgroups per XCD
+// (head 2,048-6,144 and tail 256-1,024 within 0.3 us of that; the head alone
+// 179.6 / 216.2 / 100.4, the tail alone 180.2 / 216.4 / 101.4).
+constexpr unsigned kSweepHeadBatch = 4096;
+constexpr unsigned kSweepTailBatch = 512;
+constexpr unsigned kSweepXcds = 8;  // accelerator complex dies of an MI355X
+__device__ inline bool sweep_edge_block() {
+  return blockIdx.x < kSweepHeadBatch || blockIdx.x + kSweepXcds * kSweepTailBatch >= gridDim.x;
+}
+
 // (v, i) beats (bv, bi) when larger, or equal with a lower index.
 __device__ inline void take_better(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) {
