@@ -178,6 +178,12 @@ int32_t router_max_slices(int32_t B, int32_t m);
 RouterPlan router_plan(int dtype, int32_t B, int32_t d, int32_t m, const void* hidden,
                        const void* W1);
 
+// Whether router stage 1 is small enough for its lean tiles to share the sweep's
+// launch in a fused round (router_tile.h).  Stage 1 then keeps the MFMA tile whose
+// sums the lean tile reproduces bit for bit, so a fused round and a separate
+// route agree exactly; larger routers use the two-group form.
+bool router_lean_tiles(const RouterPlan& plan, int32_t B, int32_t m);
+
 hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, const HiddenSel& sel,
                                 int dtype, int32_t B, int32_t d, const void* W1, int32_t m,
                                 float* zp, hipStream_t stream, ZeroFill zero = ZeroFill{nullptr, 0});

@@ -177,6 +177,13 @@ hipError_t launch_router_sweep_nb(unsigned grid, int nb, const void* hidden, int
 
 }  // namespace
 
+bool router_lean_tiles(const RouterPlan& plan, int32_t B, int32_t m) {
+  if (WF_ROUTER_INTERLEAVE <= 0 || !plan.mfma || plan.kslice % kLeanChunk != 0) return false;
+  const int64_t tiles = static_cast<int64_t>((m + kTileJ - 1) / kTileJ) *
+                        ((B + kTileB - 1) / kTileB) * plan.slices;
+  return tiles * (plan.kslice / kLeanChunk) <= WF_ROUTER_INTERLEAVE_LOADS;
+}
+
 bool round_stage1_fused(const RouterPlan& plan, int hidden_dtype, const void* hidden, int32_t B,
                         int32_t d, const void* W1) {
   const int per_h = hidden_dtype == WF_BF16 ? 8 : 4;
@@ -241,14 +248,12 @@ hipError_t launch_round_stage1(bool fused, const RouterPlan& plan, int hidden_dt
                                hipStream_t stream) {
   const int64_t router_gx = (static_cast<int64_t>(m) + kWaves - 1) / kWaves;
   const int64_t sweep_blocks = static_cast<int64_t>(rows) * sp.splits;
-  if (WF_ROUTER_INTERLEAVE > 0 && plan.mfma && plan.kslice % kLeanChunk == 0) {
+  if (router_lean_tiles(plan, B, m)) {
     // Router tiles padded to a whole number per XCD; the padding tiles do nothing.
     const int64_t tiles = static_cast<int64_t>((m + kTileJ - 1) / kTileJ) *
                           ((B + kTileB - 1) / kTileB) * plan.slices;
-    const int64_t loads = tiles * (plan.kslice / kLeanChunk);
     const int64_t r = (tiles + kXcdCount - 1) / kXcdCount;
-    if (loads <= WF_ROUTER_INTERLEAVE_LOADS && sweep_blocks + kXcdCount * r <= INT32_MAX &&
-        sweep_blocks / kXcdCount >= r) {
+    if (sweep_blocks + kXcdCount * r <= INT32_MAX && sweep_blocks / kXcdCount >= r) {
       return logits_dtype == WF_BF16
                  ? launch_router_mfma_sweep<WF_BF16>(plan, hidden, B, d, W1, m, zp, logits,
                                                      row_stride, rows, V, sp, part, r, stream)

@@ -13,6 +13,9 @@
 //     size across workgroups keeps every CU busy: at 256 sequences of
 //     2560 -> 1024, two slices give 256 workgroups of 96 rows x 1280 columns
 //     (240 KiB of operands each, not 480 KiB).
+//   - router_mfma2_kernel: the same tile and slice worked by two groups of four
+//     waves on alternate chunks, for routers too large to share the sweep's
+//     launch in a fused round.
 // Stage 2, router_finish_kernel, one workgroup per sequence: sums the KS
 // partials, adds b1, applies GELU and W2, sums over j and adds b2, all in
 // float32 and in a fixed order (bitwise reproducible), then thresholds.
@@ -212,6 +215,120 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
   }
 }
 
+// The same tile and slice with two groups of four waves (512 threads): group g
+// stages and multiplies the slice's chunks g, g + 2, g + 4, ... into a partial
+// tile of its own, through two LDS buffers of its own, so each barrier lets two
+// chunks proceed; the two partial tiles are added at the end (group 0's plus
+// group 1's).  The chunk time of the one-group kernel is the chain wait -> LDS
+// writes -> barrier -> LDS reads -> MFMAs that its waves walk in step; two
+// groups overlap two such chains.  Kernel trace, 256 sequences of 2560 -> 1024,
+// operands evicted, two runs each: 8.58-8.60 -> 7.96-8.00 us.  Its sums are
+// ordered differently from router_mfma_kernel's, which the shared launch's lean
+// tile reproduces, so it serves only routers too large for that launch.
+template <int NCH>
+__global__ __launch_bounds__(2 * kThreads) void router_mfma2_kernel(
+    const unsigned short* __restrict__ hidden, HiddenSel sel, int B, int d,
+    const unsigned short* __restrict__ W1, int m, int kslice, float* __restrict__ zp,
+    ZeroFill zero) {
+  static_assert(NCH > 0, "the chunk loop is unrolled whole");
+  typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
+  zero_fill_first_block(zero);
+  __shared__ __attribute__((aligned(16))) unsigned short stage[4][kStageRows * kStageStride];
+  const int tid = threadIdx.x & (kThreads - 1), grp = threadIdx.x / kThreads;
+  const int lane = tid & 63, w = tid >> 6;
+  const int j0 = blockIdx.x * kMfmaTileJ, bb0 = blockIdx.y * kMfmaTileB, slice = blockIdx.z;
+  const int k0 = slice * kslice, k1 = min(d, k0 + kslice);
+  const int r = lane & 15, g = lane >> 4;
+  const int a = w & 1, bq = (w >> 1) * 2;
+  const int prow = tid >> 4, pcol = (tid & 15) * 8;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const unsigned short* src[kPiecesPerThread];
+  bool live[kPiecesPerThread];
+#pragma unroll
+  for (int i = 0; i < kPiecesPerThread; ++i) {
+    const int row = i * 16 + prow;
+    if (row < kMfmaTileJ) {
+      live[i] = j0 + row < m;
+      src[i] = live[i] ? W1 + static_cast<int64_t>(j0 + row) * d : W1;
+    } else {
+      const int b = bb0 + row - kMfmaTileJ;
+      const int64_t h = b < B ? hidden_row(sel, b) : -1;
+      live[i] = h >= 0;
+      src[i] = live[i] ? hidden + h * d : W1;
+    }
+  }
+  const int nreal = (k1 - k0 + kChunk - 1) / kChunk;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  auto in_range = [&](int c, int i) { return live[i] && c < nreal && k0 + c * kChunk + pcol < k1; };
+  auto load = [&](int c, u32x4 (&slot)[kPiecesPerThread]) {
+#pragma unroll
+    for (int i = 0; i < kPiecesPerThread; ++i) {
+      const int k = in_range(c, i) ? k0 + c * kChunk + pcol : 0;
+      slot[i] = *reinterpret_cast<global_u32x4*>(reinterpret_cast<uintptr_t>(src[i] + k));
+    }
+  };
+  constexpr int kSteps = (NCH + 1) / 2;  // steps of two chunks, one per group
+  constexpr int kGroupRing = 2;          // chunks of a group in flight
+  u32x4 ring[kGroupRing][kPiecesPerThread];
+#pragma unroll
+  for (int q = 0; q < kGroupRing; ++q) load(2 * q + grp, ring[q]);
+#pragma unroll
+  for (int step = 0; step < kSteps; ++step) {
+    const int q = step % kGroupRing;
+    const int c = 2 * step + grp;
+    // A group rewrites a buffer two steps after it last read it, and every wave
+    // has passed the barrier in between.
+    unsigned short* st = stage[grp * 2 + (step & 1)];
+#pragma unroll
+    for (int i = 0; i < kPiecesPerThread; ++i)
+      *reinterpret_cast<u32x4*>(&st[(i * 16 + prow) * kStageStride + pcol]) =
+          in_range(c, i) ? ring[q][i] : zero4;
+    __syncthreads();
+    if (c + 2 * kGroupRing < 2 * kSteps) load(c + 2 * kGroupRing, ring[q]);
+    if (c >= nreal) continue;  // an odd chunk count: group 1's last step is empty
+#pragma unroll
+    for (int stp = 0; stp < kChunk / 32; ++stp) {
+      const int col = stp * 32 + g * 8;
+      const bf16x8 fa = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(&st[(a * 16 + r) * kStageStride + col]));
+      const bf16x8 f0 = __builtin_bit_cast(
+          bf16x8,
+          *reinterpret_cast<const u32x4*>(&st[(kMfmaTileJ + bq * 16 + r) * kStageStride + col]));
+      const bf16x8 f1 = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(
+                      &st[(kMfmaTileJ + (bq + 1) * 16 + r) * kStageStride + col]));
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f1, acc1, 0, 0, 0);
+    }
+  }
+  // Group 1 hands its partial tile to group 0 through the first buffer.
+  __syncthreads();
+  f32x4* handoff = reinterpret_cast<f32x4*>(&stage[0][0]);
+  if (grp == 1) {
+    handoff[(w * 2 + 0) * 64 + lane] = acc0;
+    handoff[(w * 2 + 1) * 64 + lane] = acc1;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  acc0 = acc0 + handoff[(w * 2 + 0) * 64 + lane];
+  acc1 = acc1 + handoff[(w * 2 + 1) * 64 + lane];
+  const int jb = j0 + a * 16 + g * 4;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int b = bb0 + (bq + q) * 16 + r;
+    if (b >= B) continue;
+    const f32x4 v = q == 0 ? acc0 : acc1;
+    float* dst = zp + (static_cast<int64_t>(slice) * B + b) * m + jb;
+    if ((m & 3) == 0 && jb + 3 < m) {
+      *reinterpret_cast<f32x4*>(dst) = v;
+      continue;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (jb + i < m) dst[i] = v[i];
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void router_finish_kernel(
     const float* __restrict__ zp, HiddenSel sel, int KS, int B, int m, const float* __restrict__ b1,
@@ -281,9 +398,20 @@ hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, cons
                     plan.slices);
     const unsigned short* h = static_cast<const unsigned short*>(hidden);
     const unsigned short* w1 = static_cast<const unsigned short*>(W1);
-#define WF_MFMA(N)                                                                              \
-  hipLaunchKernelGGL(router_mfma_kernel<N>, grid, dim3(kThreads), 0, stream, h, sel, B, d, w1, m, \
-                     plan.kslice, zp, zero)
+    // Two groups pay from 8 chunks per slice on; at 5 the final hand-off costs more
+    // than the overlap saves (bench kernel trace, 128 sequences of 2560 -> 1024:
+    // 5.76-5.88 -> 6.00 us; 256 of 4096 -> 512, 8 chunks: 8.04-8.28 -> 7.60-7.76 us;
+    // 256 of 2560 -> 1024, 10 chunks: 8.96-9.36 -> 8.36-8.40 us).
+    const bool two = !router_lean_tiles(plan, B, m) && plan.kslice / kChunk >= 8;
+#define WF_MFMA(N)                                                                               \
+  do {                                                                                           \
+    if (two)                                                                                     \
+      hipLaunchKernelGGL(router_mfma2_kernel<N>, grid, dim3(2 * kThreads), 0, stream, h, sel, B, \
+                         d, w1, m, plan.kslice, zp, zero);                                      \
+    else                                                                                         \
+      hipLaunchKernelGGL(router_mfma_kernel<N>, grid, dim3(kThreads), 0, stream, h, sel, B, d,   \
+                         w1, m, plan.kslice, zp, zero);                                         \
+  } while (0)
     // The chunk counts of the usual slicings (2,560 or 4,096 wide hidden states
     // at 9 to 65,535 sequences); any other count takes the run-time loop.
     switch (plan.kslice / kChunk) {
@@ -297,7 +425,10 @@ hipError_t launch_router_stage1(const RouterPlan& plan, const void* hidden, cons
       case 16: WF_MFMA(16); break;
       case 20: WF_MFMA(20); break;
       case 32: WF_MFMA(32); break;
-      default: WF_MFMA(0); break;
+      default:  // a run-time chunk count: the one-group kernel's loop
+        hipLaunchKernelGGL(router_mfma_kernel<0>, grid, dim3(kThreads), 0, stream, h, sel, B, d,
+                           w1, m, plan.kslice, zp, zero);
+        break;
     }
 #undef WF_MFMA
     return hipGetLastError();

@@ -183,9 +183,14 @@ def test_router_small(dtype, B, d, m):
 
 # bf16 routers on MFMA tiles whose slicing of the hidden size gives chunk counts per slice
 # of 16, 32, 6 and 7 (the last two with a shorter last slice: 2 of 6 and 6 of 7 chunks),
-# and 9 (a count the kernel reads at run time).
+# and 9 (a count the kernel reads at run time).  The routers too large to share the
+# sweep's launch with 8 or more chunks per slice run on two wave groups: 16 and 32 chunks
+# above, and 8 chunks with a shorter last slice (128 x 3592 -> 1024: slices of 1024
+# columns, the fourth holding 520, five chunks, the last of 8 columns) and 10 chunks whose
+# last chunk is cut (256 x 2504 -> 1024: the second slice holds 1224 columns).
 @pytest.mark.parametrize("B,d,m", [(512, 4096, 512), (512, 4096, 1024), (128, 4096, 640),
-                                   (150, 2560, 704), (300, 1152, 1024)])
+                                   (150, 2560, 704), (300, 1152, 1024), (128, 3592, 1024),
+                                   (256, 2504, 1024)])
 def test_router_mfma_slicings(B, d, m):
     print(f"router MFMA slicing B={B} d={d} m={m}", flush=True)
     r = make_router_inputs(B * 7 + d + m, B, d, m, "bf16")
