@@ -103,22 +103,23 @@ def test_sweep_workload_full_size():
     _check_chunks(batch.logits, "bf16", vals, idx, rows=sample)
 
 
-@pytest.mark.parametrize("B", [161, 240])
-def test_sweep_large_launch_edges(B):
+@pytest.mark.parametrize("dtype,B", [("bf16", 161), ("bf16", 240), ("f32", 240)])
+def test_sweep_large_launch_edges(dtype, B):
     """Launches just past the small-launch limit of 8,192 workgroups, where the first 4,096
     workgroups and the last 512 of each XCD issue their loads in one batch and the rest one
     at a time: 161 chains of 17 rows over 20,011 entries (3 chunks a row, 8,211 workgroups,
-    19 streaming ones) and 240 chains (12,240 workgroups, 4,048 streaming)."""
-    print(f"sweep large-launch edges B={B}", flush=True)
+    19 streaming ones) and 240 chains (12,240 workgroups, 4,048 streaming), in bfloat16 and
+    float32."""
+    print(f"sweep large-launch edges dtype={dtype} B={B}", flush=True)
     V = 20011
-    cb = make_chain_batch(40 + B, B, 16, V, "bf16")
+    cb = make_chain_batch(40 + B, B, 16, V, dtype)
     raw = cb.logits
     chunks, _ = wf.argmax_sweep_plan(raw.shape[0], V)
     assert raw.shape[0] * chunks > 8192
-    vals, idx = _run(raw, "bf16", V + 5)
-    assert np.array_equal(_merged(vals, idx), oracle.row_argmax(raw, "bf16"))
+    vals, idx = _run(raw, dtype, V + 5)
+    assert np.array_equal(_merged(vals, idx), oracle.row_argmax(raw, dtype))
     sample = np.random.default_rng(B).choice(raw.shape[0], 48, replace=False)
-    _check_chunks(raw, "bf16", vals, idx, rows=sample)
+    _check_chunks(raw, dtype, vals, idx, rows=sample)
 
 
 @pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 20011), ("bf16", 2049)])
